@@ -1,0 +1,153 @@
+/*
+ * attn.h - C-ABI of the MI355X (gfx950) fused scaled-dot-product attention engine.
+ *
+ * The operation is the one the three pages turn on:
+ *   TransformerEngine pull request 3527, "cuDNN FROST attention backend for head_dim in (256, 512],
+ *   with context parallelism" - sections Approach, Verification and Scope: fused attention
+ *   S = scale * Q K^T, one of the masks no_mask / causal / causal_bottom_right, softmax, O = P V,
+ *   and a backward producing dQ, dK, dV; symmetric head dims; GQA and MHA; bshd-style layouts.
+ *   TransformerEngine pull request 3705 (FROST forward provider for context-parallel attention) -
+ *   section Execution and supported scope: compact packed (THD) batches described by zero-based
+ *   cumulative sequence lengths with no holes, checked on the device on every execution; the
+ *   forward returns fp32 Stats that are natural logarithms, token-major for packed batches, and
+ *   the backward consumes them; operand/workspace alignment, capacity and overlap are validated;
+ *   the caller binds pointers, workspace and stream on every call.
+ *   TransformerEngine pull request 3693, "Switch to Python binding for cuDNN frontend" - review
+ *   comments on the fused-attention wrapper: Stats are [tq, h] for packed inputs and [b, h, sq]
+ *   for dense ones; the attention scale is an fp32 value passed by value.
+ *
+ * Ownership: the caller allocates every buffer (inputs, outputs, workspace). The library allocates
+ * nothing, frees nothing, never synchronises, keeps no pointer after a call returns and holds no
+ * global mutable state apart from a thread-local error string. Calls on different streams are
+ * independent as long as their outputs and workspaces are distinct.
+ *
+ * Errors: every problem that is knowable on the host is reported before any launch, as a status
+ * code with a reason in attn_last_error(); nothing is written in that case. An unsupported
+ * feature is ATTN_E_UNSUPPORTED, never a silent fallback to another computation. HIP launch
+ * failures are ATTN_E_HIP (read with hipGetLastError, no synchronisation). Malformed packed
+ * sequence lengths (only visible on the device) set the workspace error word (see below) and the
+ * kernels then fill every output with NaN. No C++ exception crosses this boundary.
+ */
+#ifndef SDPA02_ATTN_H
+#define SDPA02_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,     /* malformed argument: null pointer, bad size, bad stride, ...       */
+  ATTN_E_UNSUPPORTED = 2, /* well-formed but outside what is built (head_dim, dtype, ...)      */
+  ATTN_E_ALIGN = 3,       /* a pointer or stride breaks the 16-byte alignment rule             */
+  ATTN_E_OVERLAP = 4,     /* an output overlaps an input, another output or the workspace     */
+  ATTN_E_WORKSPACE = 5,   /* workspace smaller than attn_*_workspace_bytes() or misaligned     */
+  ATTN_E_HIP = 6          /* a kernel launch failed                                            */
+} attn_status_t;
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
+
+/* Mask vocabulary of pull request 3527, section Scope. For query i and key j of one sequence
+ * (both zero-based, lengths Sq and Skv):
+ *   ATTN_MASK_NONE       every key is allowed
+ *   ATTN_MASK_CAUSAL_TL  causal, top-left aligned:     allowed iff j <= i
+ *   ATTN_MASK_CAUSAL_BR  causal, bottom-right aligned: allowed iff j <= i + (Skv - Sq)
+ * The bottom-right band is what a context-parallel rank holding the last Sq queries of a sequence
+ * needs on its trimmed KV range (pull request 3527, section Approach). A query row with no allowed
+ * key gets O = 0, LSE = -inf and a zero gradient. */
+typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL_TL = 1, ATTN_MASK_CAUSAL_BR = 2 } attn_mask_t;
+
+/* One attention problem. All tensors have a contiguous head dimension (stride 1).
+ *
+ * Dense batches (cu_seqlens_q == cu_seqlens_kv == NULL): Q, O, dO, dQ are logically [B, Sq, Hq, D]
+ * and K, V, dK, dV are [B, Skv, Hkv, D], with element strides (batch, sequence, head) given in
+ * *_stride[0..2]; Sq = max_seqlen_q, Skv = max_seqlen_kv for every batch element. This covers
+ * bshd, sbhd and bhsd storage. LSE is contiguous fp32 [B, Hq, Sq].
+ *
+ * Packed (THD) batches (both cu_seqlens non-NULL): Q, O, dO, dQ are [total_q, Hq, D] and K, V, dK,
+ * dV are [total_kv, Hkv, D], with strides (token, head) in *_stride[0..1] (index 2 unused).
+ * Sequence b owns tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (and likewise for K/V); both
+ * arrays are device int32[batch + 1], zero-based, non-decreasing, ending at total_q / total_kv,
+ * with every sequence length <= max_seqlen_q / max_seqlen_kv and a non-empty KV range wherever the
+ * query range is non-empty. LSE is contiguous fp32 [total_q, Hq] (token-major).
+ *
+ * Grouped-query attention: q-head h reads kv-head h / (heads_q / heads_kv).
+ * dQ/dK/dV use the strides of Q/K/V; dO uses the strides of O. */
+typedef struct attn_problem {
+  int32_t abi_version; /* must be ATTN_ABI_VERSION                                   */
+  int32_t dtype;       /* attn_dtype_t: element type of Q, K, V, O, dO, dQ, dK, dV    */
+  int32_t mask;        /* attn_mask_t                                                 */
+  float scale;         /* multiplies Q K^T before masking and softmax (1/sqrt(D) usually) */
+  int32_t batch;       /* dense batch size or number of packed sequences (>= 0)       */
+  int32_t heads_q;     /* Hq >= 1                                                     */
+  int32_t heads_kv;    /* Hkv >= 1, Hq % Hkv == 0                                     */
+  int32_t head_dim;    /* D in {64, 128, 256, 512}                                    */
+  int32_t max_seqlen_q;  /* dense: Sq; packed: an upper bound of every query length   */
+  int32_t max_seqlen_kv; /* dense: Skv; packed: an upper bound of every key length    */
+  const int32_t* cu_seqlens_q;  /* device int32[batch + 1] or NULL (dense)            */
+  const int32_t* cu_seqlens_kv; /* device int32[batch + 1] or NULL (dense)            */
+  int64_t total_q;     /* packed: cu_seqlens_q[batch] (tokens in Q); dense: ignored   */
+  int64_t total_kv;    /* packed: cu_seqlens_kv[batch]; dense: ignored                */
+  int64_t q_stride[3]; /* element strides, see above                                  */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} attn_problem_t;
+
+/* Workspace. Its first 256 bytes are a header whose int32 at offset 0 is the device error word:
+ * 0 after a call whose packed sequence lengths were valid, otherwise a nonzero code (bit 0: first
+ * offset not zero; bit 1: decreasing offsets; bit 2: last offset differs from total_q/total_kv;
+ * bit 3: a length exceeds max_seqlen; bit 4: queries without keys). The word is written by every
+ * call (no pre-clearing needed). Dense forward calls need no workspace (0 bytes; ws may be NULL).
+ * The backward workspace is linear in the number of query tokens: header + two fp32 [Hq x tokens]
+ * arrays (row sums D = rowsum(dO * O), and LSE in log2 units). Sizes are multiples of 256. */
+size_t attn_fwd_workspace_bytes(const attn_problem_t* p);
+size_t attn_bwd_workspace_bytes(const attn_problem_t* p);
+
+/* Forward: O = softmax(mask(scale * Q K^T)) V and LSE = log(sum_j exp(S_ij)) (natural log, fp32).
+ * q, k, v: device inputs in p->dtype; o: device output (O's strides); lse: device fp32 output;
+ * ws: device workspace of ws_bytes >= attn_fwd_workspace_bytes(p), 256-byte aligned;
+ * stream: the hipStream_t to launch on (NULL = the default stream). Pointers and strides must
+ * be 16-byte aligned (strides multiples of 8 elements); lse 4-byte aligned. */
+attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, const void* v, void* o,
+                       float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward from the saved LSE: given dO, returns dQ, dK, dV of the forward above.
+ * o and lse must be the forward's outputs for the same q, k, v (O is used for the row sums
+ * D = rowsum(dO * O)); d_o uses O's strides. dK and dV of kv-head g sum over the q-heads of
+ * g's group. Every element of dq, dk, dv is written (keys that no query sees get zeros). */
+attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                       const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* The three passes attn_bwd runs, in this order, as separate calls with attn_bwd's arguments
+ * (each validates the whole argument list the same way). The backward is defined by the method as
+ * these steps: preprocess D = rowsum(dO * O) (and LSE in log2 units, +inf for rows with no key)
+ * into the workspace, writing the error word for packed batches; the dK/dV pass, which writes dk
+ * and dv; the dQ pass, which writes dq. dkdv and dq read what preprocess left in the same workspace
+ * for the same problem and inputs, so they must follow it on the same stream (or after an event);
+ * they are independent of each other. Splitting them lets a caller time or overlap the passes. */
+attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                                  const void* o, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
+                                  void* ws, size_t ws_bytes, void* stream);
+attn_status_t attn_bwd_dkdv(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                            const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream);
+attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                          const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                          size_t ws_bytes, void* stream);
+
+const char* attn_status_str(attn_status_t s); /* static string naming the status code          */
+const char* attn_last_error(void);            /* thread-local reason for this thread's last error */
+int32_t attn_abi_version(void);               /* ATTN_ABI_VERSION of the built library           */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA02_ATTN_H */

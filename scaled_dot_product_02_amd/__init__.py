@@ -1,0 +1,20 @@
+"""MI355X (gfx950) fused scaled-dot-product attention engine.
+
+The hot path (forward, backward preprocess, dK/dV pass, dQ pass) is hand-written
+HIP in csrc/, behind the C-ABI of include/attn.h, built into libsdpa02.so. This
+package exposes that ABI to Python under the same names (argument marshalling
+only) plus the seeded synthetic workloads used by the tests and bench.py.
+"""
+
+from ._binding import (  # noqa: F401
+    ABI_VERSION,
+    AttnError,
+    AttnProblem,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
+    attn_fwd,
+    attn_fwd_workspace_bytes,
+    lib,
+    library_path,
+    make_problem,
+)

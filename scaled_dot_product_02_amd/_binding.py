@@ -1,0 +1,237 @@
+"""ctypes binding of the C-ABI in include/attn.h (argument marshalling only).
+
+Every step of attention runs in the HIP kernels of libsdpa02.so. This module
+only turns torch tensors (device memory) and the current torch stream into the
+pointers, strides and sizes the C entry points take, allocates outputs and
+workspace with torch when the caller does not pass them, and raises AttnError
+with the library's status and reason when a call is declined. There is no
+fallback: if the library is missing, the first call raises.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libsdpa02.so"
+
+ABI_VERSION = 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
+          5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
+MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_workspace_bytes",
+            "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error", "attn_abi_version")
+BWD_PASSES = {"all": "attn_bwd", "preprocess": "attn_bwd_preprocess", "dkdv": "attn_bwd_dkdv", "dq": "attn_bwd_dq"}
+
+
+class AttnProblem(ctypes.Structure):
+    """Mirror of attn_problem_t."""
+    _fields_ = [
+        ("abi_version", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("mask", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("batch", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_kv", ctypes.c_int32),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_kv", ctypes.c_void_p),
+        ("total_q", ctypes.c_int64),
+        ("total_kv", ctypes.c_int64),
+        ("q_stride", ctypes.c_int64 * 3),
+        ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, reason):
+        self.status = status
+        self.status_name = STATUS.get(status, f"status {status}")
+        self.reason = reason
+        super().__init__(f"{self.status_name}: {reason}")
+
+
+_LIB = None
+
+
+def library_path():
+    return os.path.join(HERE, LIB_NAME)
+
+
+def lib():
+    """Load libsdpa02.so once. Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build() or "
+                               "python -m scaled_dot_product_02_amd.build")
+        L = ctypes.CDLL(path)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        pp = ctypes.POINTER(AttnProblem)
+        L.attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_fwd.restype = ctypes.c_int
+        for name in BWD_PASSES.values():
+            getattr(L, name).argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            getattr(L, name).restype = ctypes.c_int
+        L.attn_fwd_workspace_bytes.argtypes = [pp]
+        L.attn_fwd_workspace_bytes.restype = sz
+        L.attn_bwd_workspace_bytes.argtypes = [pp]
+        L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_status_str.argtypes = [ctypes.c_int]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        L.attn_abi_version.argtypes = []
+        L.attn_abi_version.restype = ctypes.c_int32
+        _LIB = L
+    return _LIB
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.bfloat16: 0, torch.float16: 1}.get(t.dtype, 99)  # 99: the library declines it
+
+
+def _strides(t, packed):
+    if t is None:
+        return (0, 0, 0)
+    st = t.stride()
+    if packed:
+        return (st[0], st[1], 0)
+    return (st[0], st[1], st[2])
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("attention tensors must be GPU tensors (the HIP kernels read them directly)")
+        if t is not None and t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous (stride 1)")
+
+
+def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv):
+    packed = cu_seqlens_q is not None
+    p = AttnProblem()
+    p.abi_version = ABI_VERSION
+    p.dtype = _dtype_code(q)
+    p.mask = MASK_CODES[mask] if isinstance(mask, str) else int(mask)
+    d = q.shape[-1]
+    p.scale = float(scale) if scale is not None else d ** -0.5
+    p.heads_q = q.shape[-2]
+    p.heads_kv = k.shape[-2]
+    p.head_dim = d
+    if packed:
+        p.batch = cu_seqlens_q.numel() - 1
+        p.total_q = q.shape[0]
+        p.total_kv = k.shape[0]
+        p.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        p.cu_seqlens_kv = cu_seqlens_kv.data_ptr()
+        if max_seqlen_q is None or max_seqlen_kv is None:
+            raise ValueError("packed batches need max_seqlen_q and max_seqlen_kv (host-known upper bounds)")
+        p.max_seqlen_q, p.max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
+    else:
+        p.batch = q.shape[0]
+        p.max_seqlen_q = q.shape[1]
+        p.max_seqlen_kv = k.shape[1]
+    p.q_stride[:] = _strides(q, packed)
+    p.k_stride[:] = _strides(k, packed)
+    p.v_stride[:] = _strides(v, packed)
+    p.o_stride[:] = _strides(o_like, packed)
+    return p
+
+
+def _raise(status):
+    L = lib()
+    raise AttnError(status, L.attn_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if nbytes == 0:
+        return workspace
+    if workspace is not None:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def attn_fwd_workspace_bytes(p):
+    return lib().attn_fwd_workspace_bytes(ctypes.byref(p))
+
+
+def attn_bwd_workspace_bytes(p):
+    return lib().attn_bwd_workspace_bytes(ctypes.byref(p))
+
+
+def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
+             max_seqlen_kv=None, out=None, lse=None, workspace=None, stream=None):
+    """Forward through the C-ABI. Returns (O, LSE).
+
+    Dense q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]; packed q [Tq,Hq,D], k/v [Tkv,Hkv,D] with int32
+    cu_seqlens on the device. LSE is fp32 [B,Hq,Sq] (dense) or [Tq,Hq] (packed).
+    """
+    import torch
+    _check_device(q, k, v, out, cu_seqlens_q, cu_seqlens_kv)
+    packed = cu_seqlens_q is not None
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        shape = (q.shape[0], q.shape[1]) if packed else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    p = make_problem(q, k, v, out, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv)
+    L = lib()
+    need = L.attn_fwd_workspace_bytes(ctypes.byref(p))
+    ws = _workspace(need, q.device, workspace)
+    st = L.attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
+                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if st != 0:
+        _raise(st)
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None,
+             max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+             passes=("all",)):
+    """Backward through the C-ABI from the forward's O and LSE. Returns (dQ, dK, dV).
+
+    dO must have O's strides; dQ/dK/dV are allocated with Q/K/V's shapes (contiguous) unless given.
+    ``passes`` lists the entry points to call in order: "all" (attn_bwd) or any of "preprocess",
+    "dkdv", "dq" (attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq, which share the workspace).
+    """
+    import torch
+    _check_device(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv)
+    if do.stride() != o.stride():
+        raise ValueError("dO must have the same strides as O")
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if dk is None:
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if dv is None:
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("dQ/dK/dV must have the strides of Q/K/V")
+    p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv)
+    L = lib()
+    need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    ws = _workspace(need, q.device, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    sptr = _stream(stream)
+    for name in passes:
+        st = getattr(L, BWD_PASSES[name])(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes, sptr)
+        if st != 0:
+            _raise(st)
+    return dq, dk, dv

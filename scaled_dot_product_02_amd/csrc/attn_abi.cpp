@@ -1,0 +1,372 @@
+// attn_abi.cpp - the C-ABI entry points of include/attn.h: host-side validation, workspace sizing
+// and kernel dispatch.
+//
+// TransformerEngine pull request 3705 (FROST forward provider for context-parallel attention),
+// section Execution and supported scope: the steady-state native path binds the current pointers,
+// workspace and stream on every call and validates operand and workspace alignment, capacity and
+// overlap before launching. Pull request 3527 ("cuDNN FROST attention backend for head_dim in
+// (256, 512], with context parallelism"), sections Notes for reviewers and Scope: unsupported
+// configurations are declined explicitly with a reason, never served by a different computation.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+constexpr size_t kHeader = 256;
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Info {
+  bool packed;
+  int64_t nq;   // query rows per head: dense batch*Sq, packed total_q
+  int64_t nkv;  // key rows per kv-head
+};
+
+// Byte extent [lo, hi) of a [seq, rows, heads, D] tensor described by strides (elements).
+struct Extent {
+  uintptr_t lo = 0, hi = 0;
+  bool empty() const { return hi <= lo; }
+};
+
+Extent extent16(const void* base, const int64_t* st, bool packed, int64_t batch, int64_t rows, int64_t heads,
+                int64_t d) {
+  Extent e;  // a NULL base still gets its size, so that check_ptr can reject it
+  if (rows <= 0 || heads <= 0 || (!packed && batch <= 0)) return e;
+  int64_t last = (rows - 1) * (packed ? st[0] : st[1]) + (heads - 1) * (packed ? st[1] : st[2]) + (d - 1);
+  if (!packed) last += (batch - 1) * st[0];
+  e.lo = (uintptr_t)base;
+  e.hi = e.lo + (uintptr_t)(last + 1) * 2;
+  return e;
+}
+
+bool overlaps(const Extent& a, const Extent& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+attn_status_t check_problem(const attn_problem_t* p, Info* info) {
+  if (!p) return fail(ATTN_E_INVALID, "problem pointer is NULL");
+  if (p->abi_version != ATTN_ABI_VERSION)
+    return fail(ATTN_E_UNSUPPORTED, "abi_version %d is not this library's %d", p->abi_version, ATTN_ABI_VERSION);
+  if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16)
+    return fail(ATTN_E_UNSUPPORTED, "dtype %d is not bf16 (0) or fp16 (1)", p->dtype);
+  if (p->mask < ATTN_MASK_NONE || p->mask > ATTN_MASK_CAUSAL_BR)
+    return fail(ATTN_E_UNSUPPORTED, "mask %d is not none (0), causal top-left (1) or causal bottom-right (2)",
+                p->mask);
+  if (p->batch < 0) return fail(ATTN_E_INVALID, "batch %d < 0", p->batch);
+  if (p->heads_q < 1 || p->heads_kv < 1) return fail(ATTN_E_INVALID, "head counts must be >= 1");
+  if (p->heads_q % p->heads_kv)
+    return fail(ATTN_E_INVALID, "heads_q %d is not a multiple of heads_kv %d", p->heads_q, p->heads_kv);
+  if (p->head_dim <= 0) return fail(ATTN_E_INVALID, "head_dim %d <= 0", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256 && p->head_dim != 512)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not built (64, 128, 256, 512)", p->head_dim);
+  if (!isfinite(p->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
+  if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
+  const bool packed = p->cu_seqlens_q != nullptr;
+  if (packed != (p->cu_seqlens_kv != nullptr))
+    return fail(ATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_kv must both be set (packed) or both be NULL");
+  if (packed) {
+    if (p->total_q < 0 || p->total_kv < 0) return fail(ATTN_E_INVALID, "negative total_q/total_kv");
+    if (p->total_q > INT32_MAX || p->total_kv > INT32_MAX)
+      return fail(ATTN_E_UNSUPPORTED, "packed totals beyond int32 offsets");
+    if (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_kv, 4))
+      return fail(ATTN_E_ALIGN, "cu_seqlens must be 4-byte aligned");
+  }
+  const int64_t* strides[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < (packed ? 2 : 3); ++i) {
+      if (strides[t][i] < 0) return fail(ATTN_E_INVALID, "%s_stride[%d] is negative", names[t], i);
+      if (strides[t][i] % 8)
+        return fail(ATTN_E_ALIGN, "%s_stride[%d] = %lld is not a multiple of 8 elements (16 bytes)", names[t], i,
+                    (long long)strides[t][i]);
+    }
+  info->packed = packed;
+  info->nq = packed ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
+  info->nkv = packed ? p->total_kv : (int64_t)p->batch * p->max_seqlen_kv;
+  return ATTN_OK;
+}
+
+Extent ext_q(const attn_problem_t* p, const void* base, const int64_t* st, bool kv, const Info& in) {
+  const int64_t rows = in.packed ? (kv ? p->total_kv : p->total_q) : (kv ? p->max_seqlen_kv : p->max_seqlen_q);
+  return extent16(base, st, in.packed, p->batch, rows, kv ? p->heads_kv : p->heads_q, p->head_dim);
+}
+
+Extent ext_lse(const attn_problem_t* p, const float* lse, const Info& in) {
+  Extent e;
+  if (in.nq <= 0) return e;
+  e.lo = (uintptr_t)lse;
+  e.hi = e.lo + (uintptr_t)(in.nq * p->heads_q) * 4;
+  return e;
+}
+
+attn_status_t check_ptr(const void* ptr, const Extent& e, const char* name) {
+  if (e.empty()) return ATTN_OK;  // nothing is read or written through it
+  if (!ptr) return fail(ATTN_E_INVALID, "%s is NULL", name);
+  if (!aligned(ptr, 16)) return fail(ATTN_E_ALIGN, "%s is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+sdpa::AttnShape make_shape(const attn_problem_t* p, const Info& in, void* ws, int qtile) {
+  sdpa::AttnShape s{};
+  s.cu_q = p->cu_seqlens_q;
+  s.cu_kv = p->cu_seqlens_kv;
+  s.err = in.packed ? (int32_t*)ws : nullptr;
+  s.batch = p->batch;
+  s.hq = p->heads_q;
+  s.hkv = p->heads_kv;
+  s.group = p->heads_q / p->heads_kv;
+  s.sq = p->max_seqlen_q;
+  s.skv = p->max_seqlen_kv;
+  s.mask = p->mask;
+  s.n_qtiles = (p->max_seqlen_q + qtile - 1) / qtile;
+  s.total_q = in.packed ? p->total_q : 0;
+  s.total_kv = in.packed ? p->total_kv : 0;
+  s.scale = p->scale;
+  s.scale_log2 = p->scale * kLog2eHost;
+  return s;
+}
+
+sdpa::TensorAddr addr(const int64_t* st, bool packed) {
+  sdpa::TensorAddr a;
+  if (packed) {
+    a.batch = 0;
+    a.row = st[0];
+    a.head = st[1];
+  } else {
+    a.batch = st[0];
+    a.row = st[1];
+    a.head = st[2];
+  }
+  return a;
+}
+
+sdpa::TensorAddr lse_addr(const attn_problem_t* p, bool packed) {
+  sdpa::TensorAddr a;
+  if (packed) {  // [total_q, Hq], token-major
+    a.batch = 0;
+    a.row = p->heads_q;
+    a.head = 1;
+  } else {  // [B, Hq, Sq]
+    a.batch = (int64_t)p->heads_q * p->max_seqlen_q;
+    a.row = 1;
+    a.head = p->max_seqlen_q;
+  }
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_E_INVALID: return "ATTN_E_INVALID";
+    case ATTN_E_UNSUPPORTED: return "ATTN_E_UNSUPPORTED";
+    case ATTN_E_ALIGN: return "ATTN_E_ALIGN";
+    case ATTN_E_OVERLAP: return "ATTN_E_OVERLAP";
+    case ATTN_E_WORKSPACE: return "ATTN_E_WORKSPACE";
+    case ATTN_E_HIP: return "ATTN_E_HIP";
+  }
+  return "ATTN_E_UNKNOWN";
+}
+
+size_t attn_fwd_workspace_bytes(const attn_problem_t* p) {
+  Info in;
+  if (check_problem(p, &in) != ATTN_OK) return 0;
+  return in.packed ? kHeader : 0;
+}
+
+size_t attn_bwd_workspace_bytes(const attn_problem_t* p) {
+  Info in;
+  if (check_problem(p, &in) != ATTN_OK) return 0;
+  return kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float));
+}
+
+attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Info in;
+    attn_status_t st = check_problem(p, &in);
+    if (st != ATTN_OK) return st;
+    const Extent eq = ext_q(p, q, p->q_stride, false, in), ek = ext_q(p, k, p->k_stride, true, in),
+                 ev = ext_q(p, v, p->v_stride, true, in), eo = ext_q(p, o, p->o_stride, false, in),
+                 el = ext_lse(p, lse, in);
+    if ((st = check_ptr(q, eq, "q")) || (st = check_ptr(k, ek, "k")) || (st = check_ptr(v, ev, "v")) ||
+        (st = check_ptr(o, eo, "o")))
+      return st;
+    if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+    if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
+    const size_t need = attn_fwd_workspace_bytes(p);
+    if (ws_bytes < need) return fail(ATTN_E_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+    if (need && (!ws || !aligned(ws, 256))) return fail(ATTN_E_WORKSPACE, "workspace NULL or not 256-byte aligned");
+    Extent ew;
+    if (need) {
+      ew.lo = (uintptr_t)ws;
+      ew.hi = ew.lo + need;
+    }
+    const Extent* ins[3] = {&eq, &ek, &ev};
+    for (const Extent* x : ins) {
+      if (overlaps(eo, *x)) return fail(ATTN_E_OVERLAP, "o overlaps an input");
+      if (overlaps(el, *x)) return fail(ATTN_E_OVERLAP, "lse overlaps an input");
+    }
+    if (overlaps(eo, el)) return fail(ATTN_E_OVERLAP, "o overlaps lse");
+    if (overlaps(ew, eo) || overlaps(ew, el) || overlaps(ew, eq) || overlaps(ew, ek) || overlaps(ew, ev))
+      return fail(ATTN_E_OVERLAP, "workspace overlaps a tensor");
+    if (p->batch == 0 || in.nq == 0) return ATTN_OK;  // no query row: nothing to write
+
+    sdpa::FwdArgs a{};
+    a.s = make_shape(p, in, ws, sdpa::fwd_query_tile(p->head_dim));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.aq = addr(p->q_stride, in.packed);
+    a.ak = addr(p->k_stride, in.packed);
+    a.av = addr(p->v_stride, in.packed);
+    a.ao = addr(p->o_stride, in.packed);
+    a.alse = lse_addr(p, in.packed);
+    if (in.packed) {
+      const int e = sdpa::launch_validate_cu(a.s, stream);
+      if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    if (a.s.n_qtiles == 0) return ATTN_OK;
+    const int e = sdpa::launch_fwd(p->dtype, p->head_dim, a, stream);
+    if (e) return fail(ATTN_E_HIP, "forward launch: %s", hipGetErrorString((hipError_t)e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_INVALID, "internal error");
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, const void* k, const void* v,
+                         const void* o, const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                         size_t ws_bytes, void* stream) {
+  try {
+    Info in;
+    attn_status_t st = check_problem(p, &in);
+    if (st != ATTN_OK) return st;
+    const Extent eq = ext_q(p, q, p->q_stride, false, in), ek = ext_q(p, k, p->k_stride, true, in),
+                 ev = ext_q(p, v, p->v_stride, true, in), eo = ext_q(p, o, p->o_stride, false, in),
+                 edo = ext_q(p, d_o, p->o_stride, false, in), el = ext_lse(p, lse, in),
+                 edq = ext_q(p, dq, p->q_stride, false, in), edk = ext_q(p, dk, p->k_stride, true, in),
+                 edv = ext_q(p, dv, p->v_stride, true, in);
+    if ((st = check_ptr(q, eq, "q")) || (st = check_ptr(k, ek, "k")) || (st = check_ptr(v, ev, "v")) ||
+        (st = check_ptr(o, eo, "o")) || (st = check_ptr(d_o, edo, "d_o")) || (st = check_ptr(dq, edq, "dq")) ||
+        (st = check_ptr(dk, edk, "dk")) || (st = check_ptr(dv, edv, "dv")))
+      return st;
+    if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+    if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
+    const size_t need = attn_bwd_workspace_bytes(p);
+    if (ws_bytes < need) return fail(ATTN_E_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+    if (!ws || !aligned(ws, 256)) return fail(ATTN_E_WORKSPACE, "workspace NULL or not 256-byte aligned");
+    Extent ew;
+    ew.lo = (uintptr_t)ws;
+    ew.hi = ew.lo + need;
+    const Extent* ins[7] = {&eq, &ek, &ev, &eo, &edo, &el, &ew};
+    const Extent* outs[3] = {&edq, &edk, &edv};
+    const char* onames[3] = {"dq", "dk", "dv"};
+    for (int i = 0; i < 3; ++i) {
+      for (const Extent* x : ins)
+        if (overlaps(*outs[i], *x)) return fail(ATTN_E_OVERLAP, "%s overlaps an input or the workspace", onames[i]);
+      for (int j = i + 1; j < 3; ++j)
+        if (overlaps(*outs[i], *outs[j])) return fail(ATTN_E_OVERLAP, "%s overlaps %s", onames[i], onames[j]);
+    }
+    for (int i = 0; i < 6; ++i)
+      if (overlaps(ew, *ins[i])) return fail(ATTN_E_OVERLAP, "workspace overlaps an input");
+    if (p->batch == 0 || (in.nq == 0 && in.nkv == 0)) return ATTN_OK;
+
+    sdpa::BwdArgs a{};
+    a.s = make_shape(p, in, ws, sdpa::bwd_query_tile(p->head_dim));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.d_o = d_o;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.nrows = in.nq;
+    a.rowsum = (float*)((char*)ws + kHeader);
+    a.lse2 = (float*)((char*)ws + kHeader + round256((size_t)in.nq * p->heads_q * sizeof(float)));
+    a.aq = addr(p->q_stride, in.packed);
+    a.ak = addr(p->k_stride, in.packed);
+    a.av = addr(p->v_stride, in.packed);
+    a.ao = addr(p->o_stride, in.packed);
+    a.alse = lse_addr(p, in.packed);
+    const int kt = sdpa::bwd_key_tile(p->head_dim);
+    a.n_kvtiles = (p->max_seqlen_kv + kt - 1) / kt;
+    if (in.packed && (passes & sdpa::kPassPre)) {
+      const int e = sdpa::launch_validate_cu(a.s, stream);
+      if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    const int e = sdpa::launch_bwd(p->dtype, p->head_dim, a, passes, stream);
+    if (e) return fail(ATTN_E_HIP, "backward launch: %s", hipGetErrorString((hipError_t)e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_INVALID, "internal error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                       const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return bwd_passes(sdpa::kPassAll, p, q, k, v, o, d_o, lse, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                                  const void* o, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return bwd_passes(sdpa::kPassPre, p, q, k, v, o, d_o, lse, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+attn_status_t attn_bwd_dkdv(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                            const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return bwd_passes(sdpa::kPassDkdv, p, q, k, v, o, d_o, lse, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                          const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return bwd_passes(sdpa::kPassDq, p, q, k, v, o, d_o, lse, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

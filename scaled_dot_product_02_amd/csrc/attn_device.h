@@ -1,0 +1,115 @@
+// attn_device.h - gfx950 (CDNA4) device primitives used by the attention kernels.
+//
+// MFMA lane layouts (wave64), checked on the hardware against a host matmul:
+//   v_mfma_f32_32x32x16_{bf16,f16}: A[row][k]: lane l holds row l%32, k = 8*(l/32) + t (t = 0..7);
+//     B[k][col]: lane l holds col l%32, k = 8*(l/32) + t; C[row][col] (16 fp32 per lane):
+//     lane l holds col l%32, rows 8*(j/4) + 4*(l/32) + (j%4) for register j = 0..15.
+//   v_mfma_f32_16x16x32_{bf16,f16}: A: lane l holds row l%16, k = 8*(l/16) + t;
+//     B: lane l holds col l%16, k = 8*(l/16) + t; C (4 fp32 per lane): col l%16, rows 4*(l/16) + i.
+// Because the contraction sums over k, any bijection between k slots and the true reduction index
+// may be used as long as A and B agree on it; the kernels use this to feed an accumulator layout
+// directly back in as the next product's operand.
+//
+// ds_read_b64_tr_b16 (LDS transpose read), as measured: within each group of 16 lanes, output
+// lane i, element r is element (i % 4) of the 8 bytes addressed by lane 4*r + i/4. So if lanes
+// 4r..4r+3 address row r of a 4 x 16 block of 16-bit values (4 consecutive elements each), lane i
+// receives column i of that block: one transposed operand fragment per instruction.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
+typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 v8bf __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 v8h __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef __bf16 v4bf __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef _Float16 v4h __attribute__((__vector_size__(4 * sizeof(_Float16))));
+typedef float v16f __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_cvoid;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element-type traits: 8-element MFMA operand, conversion from fp32 and the two MFMA shapes.
+template <typename T> struct Elem;
+
+template <> struct Elem<__bf16> {
+  typedef v8bf op8;
+  typedef v4bf op4;
+  static __device__ __forceinline__ op8 cast(v8s x) { return __builtin_bit_cast(op8, x); }
+  static __device__ __forceinline__ __bf16 cvt(float f) { return (__bf16)f; }
+  static __device__ __forceinline__ v16f mma32(op8 a, op8 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4f mma16(op8 a, op8 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Elem<_Float16> {
+  typedef v8h op8;
+  typedef v4h op4;
+  static __device__ __forceinline__ op8 cast(v8s x) { return __builtin_bit_cast(op8, x); }
+  static __device__ __forceinline__ _Float16 cvt(float f) { return (_Float16)f; }
+  static __device__ __forceinline__ v16f mma32(op8 a, op8 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4f mma16(op8 a, op8 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// 8 fp32 values -> one 8-element operand (round to nearest even).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::op8 pack8(float f0, float f1, float f2, float f3, float f4, float f5,
+                                                       float f6, float f7) {
+  typename Elem<T>::op8 r;
+  r[0] = Elem<T>::cvt(f0); r[1] = Elem<T>::cvt(f1); r[2] = Elem<T>::cvt(f2); r[3] = Elem<T>::cvt(f3);
+  r[4] = Elem<T>::cvt(f4); r[5] = Elem<T>::cvt(f5); r[6] = Elem<T>::cvt(f6); r[7] = Elem<T>::cvt(f7);
+  return r;
+}
+
+// 16 bytes from LDS (element offset, 16-bit elements).
+__device__ __forceinline__ v8s lds_read16(const unsigned short* base, int elem) {
+  return *reinterpret_cast<const v8s*>(base + elem);
+}
+
+// Transposed 8-byte LDS read (see the header comment for the lane mapping).
+__device__ __forceinline__ v4s lds_read_tr(const unsigned short* base, int elem) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(base + elem));
+}
+
+__device__ __forceinline__ v8s cat44(v4s a, v4s b) {
+  v8s r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4). The LDS destination is
+// wave-uniform: lane l's 16 bytes land at lds_wave_base + 16*l.
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_cvoid*)g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+// Same with 4 bytes per lane (lane l's dword lands at lds_wave_base + 4*l).
+__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_cvoid*)g, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including LDS DMA) have landed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Swizzled position of 16-byte chunk c of row r in an LDS tile with `chunks` chunks per row:
+// XOR with the row's low 3 bits spreads 8 consecutive rows over 8 distinct bank groups.
+__device__ __forceinline__ int swz(int r, int c, int chunks) { return r * chunks * 8 + ((c ^ (r & 7)) << 3); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+}  // namespace sdpa

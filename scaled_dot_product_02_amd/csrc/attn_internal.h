@@ -1,0 +1,69 @@
+// attn_internal.h - parameter blocks passed from the host dispatcher (attn_abi.cpp) to the
+// kernels (attn_kernels.hip). Not part of the public ABI.
+#pragma once
+#include <stdint.h>
+
+namespace sdpa {
+
+// Addressing of one [sequence, head, D] tensor. Element (b, s, h, d) of a dense tensor lives at
+// base + b*batch + s*row + h*head + d; for a packed tensor the sequence start token cu[b] replaces
+// the batch term: base + (cu[b] + s)*row + h*head + d.
+struct TensorAddr {
+  int64_t batch;
+  int64_t row;
+  int64_t head;
+};
+
+struct AttnShape {
+  const int32_t* cu_q;   // device, packed batches only (else nullptr)
+  const int32_t* cu_kv;  // device, packed batches only (else nullptr)
+  int32_t* err;          // device error word (packed batches) or nullptr
+  int32_t batch, hq, hkv, group;  // group = hq / hkv
+  int32_t sq, skv;                // dense lengths, or the host-side maxima for packed batches
+  int32_t mask;                   // attn_mask_t
+  int32_t n_qtiles;               // ceil(sq / query tile) of the launched kernel
+  int64_t total_q, total_kv;      // packed token counts (for NaN fill on device errors)
+  float scale;                    // softmax scale
+  float scale_log2;               // scale * log2(e)
+};
+
+struct FwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  TensorAddr aq, ak, av, ao;
+  TensorAddr alse;  // LSE addressing (d term absent)
+};
+
+struct BwdArgs {
+  AttnShape s;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* d_o;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* rowsum;  // workspace: D = rowsum(dO * O), [hq][nrows]
+  float* lse2;    // workspace: LSE * log2(e) (+inf for empty rows), [hq][nrows]
+  int64_t nrows;  // dense: batch * sq; packed: total_q
+  TensorAddr aq, ak, av, ao, alse;
+  int32_t n_kvtiles;  // ceil(skv / key tile) of the dK/dV kernel
+};
+
+// Launchers (attn_kernels.hip). Return hipError_t as int.
+int launch_validate_cu(const AttnShape& s, void* stream);
+int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream);
+// Backward passes selected by bit: 1 = preprocess, 2 = dK/dV pass, 4 = dQ pass.
+enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassAll = 7 };
+int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream);
+int fwd_query_tile(int head_dim);
+int bwd_key_tile(int head_dim);
+int bwd_query_tile(int head_dim);
+
+}  // namespace sdpa

@@ -1,0 +1,720 @@
+// attn_kernels.hip - fused scaled-dot-product attention, forward and backward, for gfx950.
+//
+// The computation (TransformerEngine pull request 3527, "cuDNN FROST attention backend for
+// head_dim in (256, 512], with context parallelism", sections Approach and Scope; pull request
+// 3705, section Execution and supported scope):
+//   forward   S = scale * Q K^T, mask, online softmax in the log2 domain, O = P V, and the per-row
+//             natural-log LSE (fp32 Stats) that the backward consumes;
+//   backward  preprocess D = rowsum(dO * O); a dK/dV pass (one workgroup per key tile, looping
+//             over the query tiles and q-heads that see it); a dQ pass (one workgroup per query
+//             tile, looping over the key tiles it sees). Both passes recompute P = exp(S - LSE)
+//             from the saved LSE. No atomics: every output element has exactly one writer, so
+//             results are deterministic.
+//
+// Masks: interior tiles take no mask; only tiles that cross the causal diagonal, the sequence
+// tails or (bottom-right) the empty-row region are masked element by element; tiles that are
+// fully masked for a whole workgroup are never loaded, and a wave skips the MFMAs of a tile that
+// is fully masked for its own rows.
+//
+// K/V (forward, dQ pass) and Q/dO (dK/dV pass) tiles are streamed HBM -> LDS with
+// global_load_lds_dwordx4 into a two-stage ring, one barrier per tile; LDS rows are XOR-swizzled
+// in 16-byte chunks. Operands whose contraction index runs along LDS rows are fetched with the
+// LDS transpose read (ds_read_b64_tr_b16).
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "attn_device.h"
+#include "attn_internal.h"
+
+namespace sdpa {
+
+typedef unsigned short us;
+
+__device__ __forceinline__ int64_t seq_off(const TensorAddr& t, bool packed, int b, int64_t tok0) {
+  return packed ? tok0 * t.row : (int64_t)b * t.batch;
+}
+
+struct Seq {
+  int sq, skv;
+  int64_t tq0, tk0;
+};
+
+__device__ __forceinline__ Seq seq_info(const AttnShape& s, int b) {
+  Seq r;
+  if (s.cu_q) {
+    const int a0 = s.cu_q[b], a1 = s.cu_q[b + 1], k0 = s.cu_kv[b], k1 = s.cu_kv[b + 1];
+    r.sq = a1 - a0;
+    r.skv = k1 - k0;
+    r.tq0 = a0;
+    r.tk0 = k0;
+  } else {
+    r.sq = s.sq;
+    r.skv = s.skv;
+    r.tq0 = 0;
+    r.tk0 = 0;
+  }
+  return r;
+}
+
+template <typename T> __device__ __forceinline__ us nan_bits();
+template <> __device__ __forceinline__ us nan_bits<__bf16>() { return 0x7FC0; }
+template <> __device__ __forceinline__ us nan_bits<_Float16>() { return 0x7E00; }
+
+template <typename T> __device__ __forceinline__ float to_f32(short x) {
+  return (float)__builtin_bit_cast(T, x);
+}
+
+__device__ __forceinline__ int64_t flat_block() {
+  return blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+}
+__device__ __forceinline__ int64_t flat_grid_threads() {
+  return (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+}
+
+// Fill a packed [tokens, heads, D] tensor with NaN (grid-stride over all workgroups).
+template <int D, typename T>
+__device__ void fill_nan_rows(void* base, const TensorAddr& a, int64_t tokens, int heads) {
+  constexpr int CH = D / 8;
+  v8s nanv;
+  for (int i = 0; i < 8; ++i) nanv[i] = (short)nan_bits<T>();
+  const int64_t n = tokens * heads * CH;
+  for (int64_t i = flat_block() * blockDim.x + threadIdx.x; i < n; i += flat_grid_threads()) {
+    const int64_t t = i / (heads * CH);
+    const int rem = (int)(i % (heads * CH));
+    *reinterpret_cast<v8s*>((us*)base + t * a.row + (int64_t)(rem / CH) * a.head + (rem % CH) * 8) = nanv;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Device check of packed sequence offsets (pull request 3705, section Execution and supported
+// scope: compactness checked on the GPU on every execution). One workgroup; writes the error
+// word unconditionally so no pre-clearing is needed.
+// ------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) validate_cu_kernel(AttnShape s) {
+  __shared__ int flag;
+  if (threadIdx.x == 0) flag = 0;
+  __syncthreads();
+  int f = 0;
+  for (int b = threadIdx.x; b < s.batch; b += blockDim.x) {
+    const int q0 = s.cu_q[b], q1 = s.cu_q[b + 1], k0 = s.cu_kv[b], k1 = s.cu_kv[b + 1];
+    if (q1 < q0 || k1 < k0) f |= 2;
+    if (q1 - q0 > s.sq || k1 - k0 > s.skv) f |= 8;
+    if (q1 > q0 && k1 == k0) f |= 16;
+  }
+  if (threadIdx.x == 0) {
+    if (s.cu_q[0] != 0 || s.cu_kv[0] != 0) f |= 1;
+    if ((int64_t)s.cu_q[s.batch] != s.total_q || (int64_t)s.cu_kv[s.batch] != s.total_kv) f |= 4;
+  }
+  if (f) atomicOr(&flag, f);
+  __syncthreads();
+  if (threadIdx.x == 0) *s.err = flag;
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward. Workgroup = 4 waves = 128 query rows of one (sequence, q-head); wave w owns rows
+// q0 + 32w .. +31. Per key tile of BN keys the wave computes S^T = K Q^T with 32x32x16 MFMAs
+// (A = K rows from LDS, B = its Q fragment held in VGPRs), so lane l holds query l%32 and half
+// of the tile's keys: the row max/sum need one cross-lane exchange (lanes l and l^32). The
+// accumulator layout of S^T is fed straight back as the B operand of O^T += V^T P^T (k slots
+// permuted consistently), with V^T fetched by transpose reads.
+// ------------------------------------------------------------------------------------------
+template <int D, int BN, typename T>
+__global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
+  constexpr int BM = 128;
+  constexpr int CH = D / 8;
+  constexpr int TILE = BN * D;               // 16-bit elements of one K or V tile
+  constexpr int NDMA = TILE * 2 / 1024 / 4;  // 16-byte DMA instructions per wave per tensor
+  static_assert(NDMA >= 1 && (TILE * 2) % 4096 == 0, "tile must split evenly over 4 waves");
+  __shared__ __attribute__((aligned(1024))) us smem[2 * 2 * TILE];
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<D, T>(a.o, a.ao, s.total_q, s.hq);
+    for (int64_t i = flat_block() * blockDim.x + threadIdx.x; i < s.total_q * s.hq; i += flat_grid_threads())
+      a.lse[(i / s.hq) * a.alse.row + (i % s.hq) * a.alse.head] = __builtin_nanf("");
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int hh = lane >> 5, lrow = lane & 31;
+  const int b = blockIdx.x / s.hq, h = blockIdx.x % s.hq, g = h / s.group;
+  const int qt = s.mask != 0 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const Seq sq = seq_info(s, b);
+  const int q0 = qt * BM;
+  if (q0 >= sq.sq) return;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BM + delta) : sq.skv;
+  const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  const us* qg = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  const int qw0 = q0 + 32 * w;
+  const int qi = qw0 + lrow;
+
+  v8s qf[D / 16];
+  {
+    const us* p = qg + (int64_t)min(qi, sq.sq - 1) * a.aq.row + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const v8s*>(p + 16 * kk);
+  }
+  v16f oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = v16f{};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+
+  auto issue = [&](int tile, int stage) {
+    us* ks = smem + stage * 2 * TILE;
+    us* vs = ks + TILE;
+    const int kv0 = tile * BN;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot = (w * NDMA + i) * 64;
+      const int L = slot + lane;
+      const int r = L / CH;
+      const int c = (L % CH) ^ (r & 7);
+      const int64_t kr = min(kv0 + r, sq.skv - 1);
+      dma16(kg + kr * a.ak.row + c * 8, ks + slot * 8);
+      dma16(vg + kr * a.av.row + c * 8, vs + slot * 8);
+    }
+  };
+
+  const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+  if (n_tiles > 0) issue(0, 0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    const us* ks = smem + (j & 1) * 2 * TILE;
+    const us* vs = ks + TILE;
+    const int kv0 = j * BN;
+    if (s.mask != 0 && kv0 > qw0 + 31 + delta) continue;  // tile fully masked for this wave
+    const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta);
+
+    v16f sacc[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      sacc[kb] = v16f{};
+      const int r = 32 * kb + lrow;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const v8s kf = lds_read16(ks, swz(r, 2 * kk + hh, CH));
+        sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
+      }
+    }
+    // online softmax, log2 domain; this lane's query is qi, its keys kv0 + 32kb + 8(jr/4) + 4hh + jr%4
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr) {
+        float x = sacc[kb][jr] * s.scale_log2;
+        if (need_mask) {
+          const int key = kv0 + 32 * kb + 8 * (jr >> 2) + 4 * hh + (jr & 3);
+          const bool ok = key < sq.skv && (s.mask == 0 || key <= qi + delta);
+          x = ok ? x : -__builtin_inff();
+        }
+        sacc[kb][jr] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr) {
+        const float p = fast_exp2(sacc[kb][jr] - m_use);
+        sacc[kb][jr] = p;
+        rs += p;
+      }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+    for (int c = 0; c < BN / 16; ++c) {
+      const int kb = c >> 1, half = c & 1;
+      const auto pb = pack8<T>(sacc[kb][8 * half + 0], sacc[kb][8 * half + 1], sacc[kb][8 * half + 2],
+                               sacc[kb][8 * half + 3], sacc[kb][8 * half + 4], sacc[kb][8 * half + 5],
+                               sacc[kb][8 * half + 6], sacc[kb][8 * half + 7]);
+      const int row1 = 32 * kb + 16 * half + 4 * (G >> 1) + rr;
+      const int row2 = row1 + 8;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int col = 32 * dt + 16 * (G & 1) + 4 * cc;
+        const int chunk = col >> 3, within = col & 7;
+        const v4s lo = lds_read_tr(vs, row1 * D + ((chunk ^ (row1 & 7)) << 3) + within);
+        const v4s hi = lds_read_tr(vs, row2 * D + ((chunk ^ (row2 & 7)) << 3) + within);
+        oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
+      }
+    }
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  if (qi < sq.sq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    T* op = (T*)a.o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head + (int64_t)qi * a.ao.row;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        typename Elem<T>::op4 v;
+        v[0] = Elem<T>::cvt(oacc[dt][4 * q4 + 0] * inv);
+        v[1] = Elem<T>::cvt(oacc[dt][4 * q4 + 1] * inv);
+        v[2] = Elem<T>::cvt(oacc[dt][4 * q4 + 2] * inv);
+        v[3] = Elem<T>::cvt(oacc[dt][4 * q4 + 3] * inv);
+        *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
+      }
+    if (hh == 0) {
+      float* lp = a.lse + seq_off(a.alse, packed, b, sq.tq0) + (int64_t)h * a.alse.head + (int64_t)qi * a.alse.row;
+      *lp = lt > 0.f ? (m_run + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward preprocess: D = rowsum(dO * O) in fp32 and LSE * log2(e) (+inf for rows with no key,
+// so that exp2(S*c - lse2) is exactly 0 there), both stored head-major [hq][nrows]. HBM-bound.
+// ------------------------------------------------------------------------------------------
+template <int D, typename T>
+__global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) return;
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int64_t total = a.nrows * s.hq;
+  const int64_t R = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  int64_t t = 0, lofs = 0;
+  int h = 0;
+  if (R < total) {
+    t = R / s.hq;
+    h = (int)(R % s.hq);
+    int64_t oofs;
+    if (packed) {
+      oofs = t * a.ao.row + (int64_t)h * a.ao.head;
+      lofs = t * a.alse.row + (int64_t)h * a.alse.head;
+    } else {
+      const int64_t bb = t / s.sq, si = t % s.sq;
+      oofs = bb * a.ao.batch + si * a.ao.row + (int64_t)h * a.ao.head;
+      lofs = bb * a.alse.batch + si * a.alse.row + (int64_t)h * a.alse.head;
+    }
+    const v8s o8 = *reinterpret_cast<const v8s*>((const us*)a.o + oofs + 8 * c);
+    const v8s d8 = *reinterpret_cast<const v8s*>((const us*)a.d_o + oofs + 8 * c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += to_f32<T>(o8[i]) * to_f32<T>(d8[i]);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (R < total && c == 0) {
+    a.rowsum[(int64_t)h * a.nrows + t] = acc;
+    const float l = a.lse[lofs];
+    a.lse2[(int64_t)h * a.nrows + t] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward dK/dV pass. Workgroup = 4 waves = BKV = 64*KB keys of one (sequence, kv-head); wave w
+// owns 16*KB keys whose K and V fragments stay in VGPRs. It loops over every q-head of the GQA
+// group and every 32-row query tile that sees its keys; Q, dO, lse2 and D of the tile stream
+// through LDS. With 16x16x32 MFMAs:
+//   S = Q K^T, dP = dO V^T   (A = Q / dO rows from LDS, B = K / V fragments): lane = key
+//   P = exp2(S*c - lse2), dS = P (dP - D)
+//   dV += P^T dO, dK += dS^T Q  (A = the P / dS accumulators as they are, B = dO / Q by transpose
+//   reads). dK is scaled once at the end; keys no query sees get exact zeros.
+// ------------------------------------------------------------------------------------------
+template <int D, int KB, typename T>
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 4, KW = 16 * KB, BKV = NW * KW, BQ = 32, CH = D / 8;
+  constexpr int QTILE = BQ * D;
+  constexpr int NDMA = QTILE * 2 / 1024 / NW;
+  static_assert(NDMA >= 1, "query tile must split over 4 waves");
+  constexpr int STAGE = 2 * QTILE + 2 * 64 * 2;  // Q, dO tiles, then lse2[64] and D[64] as floats
+  __shared__ __attribute__((aligned(1024))) us smem[2 * STAGE];
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<D, T>(a.dk, a.ak, s.total_kv, s.hkv);
+    fill_nan_rows<D, T>(a.dv, a.av, s.total_kv, s.hkv);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
+  const int b = blockIdx.x / s.hkv, g = blockIdx.x % s.hkv;
+  const Seq sq = seq_info(s, b);
+  const int k0 = blockIdx.y * BKV;
+  if (k0 >= sq.skv) return;
+  const int kw0 = k0 + w * KW;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int q_lo = s.mask != 0 ? max(0, k0 - delta) : 0;
+  const int qt0 = q_lo / BQ;
+  const int nq = max(0, (sq.sq + BQ - 1) / BQ - qt0);
+  const int n_it = nq * s.group;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
+
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  v8s kf[KB][D / 32], vf[KB][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int64_t r = min(kw0 + 16 * kb + l16, sq.skv - 1);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      kf[kb][kk] = *reinterpret_cast<const v8s*>(kg + r * a.ak.row + 32 * kk + 8 * G);
+      vf[kb][kk] = *reinterpret_cast<const v8s*>(vg + r * a.av.row + 32 * kk + 8 * G);
+    }
+  }
+  v4f dk[KB][D / 16], dv[KB][D / 16];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      dk[kb][dt] = v4f{};
+      dv[kb][dt] = v4f{};
+    }
+
+  auto issue = [&](int it, int stage) {
+    const int hi = it / nq, qt = qt0 + it % nq;
+    const int h = g * s.group + hi;
+    const int qs0 = qt * BQ;
+    us* qs = smem + stage * STAGE;
+    us* dos = qs + QTILE;
+    float* l2s = reinterpret_cast<float*>(dos + QTILE);
+    float* rss = l2s + 64;
+    const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
+    const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot = (w * NDMA + i) * 64;
+      const int L = slot + lane;
+      const int r = L / CH;
+      const int c = (L % CH) ^ (r & 7);
+      const int64_t qr = min(qs0 + r, sq.sq - 1);
+      dma16(qgh + qr * a.aq.row + c * 8, qs + slot * 8);
+      dma16(dgh + qr * a.ao.row + c * 8, dos + slot * 8);
+    }
+    const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
+    if (w == 0) dma4(a.lse2 + row, l2s);
+    if (w == 1) dma4(a.rowsum + row, rss);
+  };
+
+  if (n_it > 0) issue(0, 0);
+  for (int it = 0; it < n_it; ++it) {
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < n_it) issue(it + 1, (it + 1) & 1);
+    const us* qs = smem + (it & 1) * STAGE;
+    const us* dos = qs + QTILE;
+    const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
+    const float* rss = l2s + 64;
+    const int qs0 = (qt0 + it % nq) * BQ;
+    if (kw0 >= sq.skv) continue;
+    if (s.mask != 0 && qs0 + BQ - 1 + delta < kw0) continue;  // no row of the tile sees these keys
+    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1);
+
+    v4f sv[2][KB], dp[2][KB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        sv[qb][kb] = v4f{};
+        dp[qb][kb] = v4f{};
+      }
+      const int r = 16 * qb + l16;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const v8s qa = lds_read16(qs, swz(r, 4 * kk + G, CH));
+        const v8s da = lds_read16(dos, swz(r, 4 * kk + G, CH));
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          sv[qb][kb] = Elem<T>::mma16(Elem<T>::cast(qa), Elem<T>::cast(kf[kb][kk]), sv[qb][kb]);
+          dp[qb][kb] = Elem<T>::mma16(Elem<T>::cast(da), Elem<T>::cast(vf[kb][kk]), dp[qb][kb]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const v4f l2 = *reinterpret_cast<const v4f*>(l2s + 16 * qb + 4 * G);
+      const v4f dr = *reinterpret_cast<const v4f*>(rss + 16 * qb + 4 * G);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = fast_exp2(sv[qb][kb][i] * s.scale_log2 - l2[i]);
+          if (need_mask) {
+            const int q = qs0 + 16 * qb + 4 * G + i;
+            const int key = kw0 + 16 * kb + l16;
+            const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
+            p = ok ? p : 0.f;
+          }
+          sv[qb][kb][i] = p;
+          dp[qb][kb][i] = p * (dp[qb][kb][i] - dr[i]);
+        }
+    }
+    typename Elem<T>::op8 pa[KB], sa[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      pa[kb] = pack8<T>(sv[0][kb][0], sv[0][kb][1], sv[0][kb][2], sv[0][kb][3], sv[1][kb][0], sv[1][kb][1],
+                        sv[1][kb][2], sv[1][kb][3]);
+      sa[kb] = pack8<T>(dp[0][kb][0], dp[0][kb][1], dp[0][kb][2], dp[0][kb][3], dp[1][kb][0], dp[1][kb][1],
+                        dp[1][kb][2], dp[1][kb][3]);
+    }
+    const int row1 = 4 * G + rr, row2 = row1 + 16;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int col = 16 * dt + 4 * cc;
+      const int chunk = col >> 3, within = col & 7;
+      const int o1 = row1 * D + ((chunk ^ (row1 & 7)) << 3) + within;
+      const int o2 = row2 * D + ((chunk ^ (row2 & 7)) << 3) + within;
+      const v8s dob = cat44(lds_read_tr(dos, o1), lds_read_tr(dos, o2));
+      const v8s qbt = cat44(lds_read_tr(qs, o1), lds_read_tr(qs, o2));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        dv[kb][dt] = Elem<T>::mma16(pa[kb], Elem<T>::cast(dob), dv[kb][dt]);
+        dk[kb][dt] = Elem<T>::mma16(sa[kb], Elem<T>::cast(qbt), dk[kb][dt]);
+      }
+    }
+  }
+
+  T* dkp = (T*)a.dk + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  T* dvp = (T*)a.dv + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kw0 + 16 * kb + 4 * G + i;
+      if (key < sq.skv) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          dkp[(int64_t)key * a.ak.row + 16 * dt + l16] = Elem<T>::cvt(dk[kb][dt][i] * s.scale);
+          dvp[(int64_t)key * a.av.row + 16 * dt + l16] = Elem<T>::cvt(dv[kb][dt][i]);
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward dQ pass. Workgroup = 4 waves = 64*QB query rows of one (sequence, q-head); wave w owns
+// 16*QB rows whose Q and dO fragments stay in VGPRs. K/V tiles of 32 keys stream through LDS.
+//   S^T = K Q^T, dP^T = V dO^T  (A = K / V rows from LDS, B = Q / dO fragments): lane = query
+//   P = exp2(S*c - lse2), dS = P (dP - D)            (lse2, D are per-lane scalars)
+//   dQ += dS K                  (A = the dS accumulators, B = K by transpose reads)
+// ------------------------------------------------------------------------------------------
+template <int D, int QB, typename T>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NW = 4, QW = 16 * QB, BMQ = NW * QW, BK = 32, CH = D / 8;
+  constexpr int KTILE = BK * D;
+  constexpr int NDMA = KTILE * 2 / 1024 / NW;
+  static_assert(NDMA >= 1, "key tile must split over 4 waves");
+  __shared__ __attribute__((aligned(1024))) us smem[2 * 2 * KTILE];
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<D, T>(a.dq, a.aq, s.total_q, s.hq);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
+  const int b = blockIdx.x / s.hq, h = blockIdx.x % s.hq, g = h / s.group;
+  const int qt = s.mask != 0 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const Seq sq = seq_info(s, b);
+  const int q0 = qt * BMQ;
+  if (q0 >= sq.sq) return;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BMQ + delta) : sq.skv;
+  const int n_tiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+  const int qw0 = q0 + w * QW;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
+
+  const us* qg = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
+  const us* dg = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  v8s qf[QB][D / 32], df[QB][D / 32];
+  float l2[QB], dr[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t r = min(qw0 + 16 * qb + l16, sq.sq - 1);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      qf[qb][kk] = *reinterpret_cast<const v8s*>(qg + r * a.aq.row + 32 * kk + 8 * G);
+      df[qb][kk] = *reinterpret_cast<const v8s*>(dg + r * a.ao.row + 32 * kk + 8 * G);
+    }
+    l2[qb] = a.lse2[(int64_t)h * a.nrows + rowbase + r];
+    dr[qb] = a.rowsum[(int64_t)h * a.nrows + rowbase + r];
+  }
+  v4f dq[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) dq[qb][dt] = v4f{};
+
+  auto issue = [&](int tile, int stage) {
+    us* ks = smem + stage * 2 * KTILE;
+    us* vs = ks + KTILE;
+    const int kv0 = tile * BK;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot = (w * NDMA + i) * 64;
+      const int L = slot + lane;
+      const int r = L / CH;
+      const int c = (L % CH) ^ (r & 7);
+      const int64_t kr = min(kv0 + r, sq.skv - 1);
+      dma16(kg + kr * a.ak.row + c * 8, ks + slot * 8);
+      dma16(vg + kr * a.av.row + c * 8, vs + slot * 8);
+    }
+  };
+
+  if (n_tiles > 0) issue(0, 0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    const us* ks = smem + (j & 1) * 2 * KTILE;
+    const us* vs = ks + KTILE;
+    const int kv0 = j * BK;
+    if (s.mask != 0 && kv0 > qw0 + QW - 1 + delta) continue;
+    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta);
+
+    v4f st[2][QB], dpt[2][QB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        st[kb][qb] = v4f{};
+        dpt[kb][qb] = v4f{};
+      }
+      const int r = 16 * kb + l16;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const v8s ka = lds_read16(ks, swz(r, 4 * kk + G, CH));
+        const v8s va = lds_read16(vs, swz(r, 4 * kk + G, CH));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          st[kb][qb] = Elem<T>::mma16(Elem<T>::cast(ka), Elem<T>::cast(qf[qb][kk]), st[kb][qb]);
+          dpt[kb][qb] = Elem<T>::mma16(Elem<T>::cast(va), Elem<T>::cast(df[qb][kk]), dpt[kb][qb]);
+        }
+      }
+    }
+    typename Elem<T>::op8 dsa[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float ds[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float p = fast_exp2(st[kb][qb][i] * s.scale_log2 - l2[qb]);
+          if (need_mask) {
+            const int q = qw0 + 16 * qb + l16;
+            const int key = kv0 + 16 * kb + 4 * G + i;
+            const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta);
+            p = ok ? p : 0.f;
+          }
+          ds[kb][i] = p * (dpt[kb][qb][i] - dr[qb]);
+        }
+      dsa[qb] = pack8<T>(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
+    }
+    const int row1 = 4 * G + rr, row2 = row1 + 16;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int col = 16 * dt + 4 * cc;
+      const int chunk = col >> 3, within = col & 7;
+      const v8s kbt = cat44(lds_read_tr(ks, row1 * D + ((chunk ^ (row1 & 7)) << 3) + within),
+                            lds_read_tr(ks, row2 * D + ((chunk ^ (row2 & 7)) << 3) + within));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) dq[qb][dt] = Elem<T>::mma16(dsa[qb], Elem<T>::cast(kbt), dq[qb][dt]);
+    }
+  }
+
+  T* dqp = (T*)a.dq + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = qw0 + 16 * qb + 4 * G + i;
+      if (q < sq.sq) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[qb][dt][i] * s.scale);
+      }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+// ------------------------------------------------------------------------------------------
+constexpr int kFwdBM = 128;
+template <int D> constexpr int fwd_bn() { return D <= 256 ? 64 : 32; }
+template <int D> constexpr int dkdv_kb() { return D <= 256 ? 2 : 1; }
+template <int D> constexpr int dq_qb() { return D <= 256 ? 2 : 1; }
+
+int fwd_query_tile(int) { return kFwdBM; }
+int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 256 ? 2 : 1); }
+int bwd_query_tile(int head_dim) { return 64 * (head_dim <= 256 ? 2 : 1); }
+
+int launch_validate_cu(const AttnShape& s, void* stream) {
+  hipLaunchKernelGGL(validate_cu_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, s);
+  return (int)hipGetLastError();
+}
+
+template <int D, typename T>
+static int fwd_t(const FwdArgs& a, hipStream_t st) {
+  const dim3 grid(a.s.batch * a.s.hq, a.s.n_qtiles);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), T>), grid, dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+template <int D, typename T>
+static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
+  // Launches with an empty grid are skipped (e.g. no query rows: only dK = dV = 0 remain to write).
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = a.nrows * a.s.hq;
+  hipError_t e = hipSuccess;
+  if ((passes & kPassPre) && rows > 0) {
+    hipLaunchKernelGGL((attn_bwd_pre_kernel<D, T>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
+  if ((passes & kPassDkdv) && a.n_kvtiles > 0) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), T>), dim3(a.s.batch * a.s.hkv, a.n_kvtiles),
+                       dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
+  if ((passes & kPassDq) && a.s.n_qtiles > 0) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), T>), dim3(a.s.batch * a.s.hq, a.s.n_qtiles), dim3(256),
+                       0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+  }
+  return (int)e;
+}
+
+int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = dtype == 0;
+  switch (head_dim) {
+    case 64: return bf ? fwd_t<64, __bf16>(a, st) : fwd_t<64, _Float16>(a, st);
+    case 128: return bf ? fwd_t<128, __bf16>(a, st) : fwd_t<128, _Float16>(a, st);
+    case 256: return bf ? fwd_t<256, __bf16>(a, st) : fwd_t<256, _Float16>(a, st);
+    case 512: return bf ? fwd_t<512, __bf16>(a, st) : fwd_t<512, _Float16>(a, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf = dtype == 0;
+  switch (head_dim) {
+    case 64: return bf ? bwd_t<64, __bf16>(a, passes, st) : bwd_t<64, _Float16>(a, passes, st);
+    case 128: return bf ? bwd_t<128, __bf16>(a, passes, st) : bwd_t<128, _Float16>(a, passes, st);
+    case 256: return bf ? bwd_t<256, __bf16>(a, passes, st) : bwd_t<256, _Float16>(a, passes, st);
+    case 512: return bf ? bwd_t<512, __bf16>(a, passes, st) : bwd_t<512, _Float16>(a, passes, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace sdpa

@@ -1,0 +1,223 @@
+"""C-ABI contract tests that need no GPU.
+
+The library must load, export every entry point include/attn.h declares, and
+decline every host-knowable problem before any HIP call, with a status code and
+a reason (pull request 3705, section Execution and supported scope: alignment,
+capacity and overlap are validated before launch; pull request 3527, Notes for
+reviewers / Scope: explicit declines with reasons, never a silent fallback).
+All pointers below are fake, aligned addresses: validation never dereferences
+them, and every call here returns before a kernel would be launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from scaled_dot_product_02_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, ALIGN, OVERLAP, WORKSPACE = 0, 1, 2, 3, 4, 5
+GiB = 1 << 30
+
+
+@pytest.fixture(scope="module")
+def L(lib_path):
+    return B.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    decl = declared_functions()
+    assert set(decl) == set(B.EXPORTED)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.attn_abi_version() == 1
+    for code, name in B.STATUS.items():
+        assert L.attn_status_str(code).decode() == name
+    assert L.attn_status_str(42).decode() == "ATTN_E_UNKNOWN"
+
+
+def dense_problem(b=2, sq=256, skv=256, hq=4, hkv=2, d=128, dtype=0, mask=1):
+    p = B.AttnProblem()
+    p.abi_version = 1
+    p.dtype, p.mask, p.scale = dtype, mask, d ** -0.5
+    p.batch, p.heads_q, p.heads_kv, p.head_dim = b, hq, hkv, d
+    p.max_seqlen_q, p.max_seqlen_kv = sq, skv
+    p.q_stride[:] = (sq * hq * d, hq * d, d)
+    p.o_stride[:] = (sq * hq * d, hq * d, d)
+    p.k_stride[:] = (skv * hkv * d, hkv * d, d)
+    p.v_stride[:] = (skv * hkv * d, hkv * d, d)
+    return p
+
+
+def packed_problem(tq=1000, tkv=1000, nseq=4, hq=4, hkv=4, d=64):
+    p = dense_problem(b=nseq, sq=600, skv=600, hq=hq, hkv=hkv, d=d)
+    p.cu_seqlens_q, p.cu_seqlens_kv = 0x7000_0000, 0x7000_1000
+    p.total_q, p.total_kv = tq, tkv
+    p.q_stride[:] = (hq * d, d, 0)
+    p.o_stride[:] = (hq * d, d, 0)
+    p.k_stride[:] = (hkv * d, d, 0)
+    p.v_stride[:] = (hkv * d, d, 0)
+    return p
+
+
+# fake, disjoint, 256-byte aligned device addresses, 1 GiB apart
+Q, K, V, O, LSE, WS, DO, DQ, DK, DV = (0x1_0000_0000 + i * GiB for i in range(10))
+
+
+def fwd(L, p, q=Q, k=K, v=V, o=O, lse=LSE, ws=WS, ws_bytes=1 << 20):
+    return L.attn_fwd(ctypes.byref(p) if p is not None else None, q, k, v, o, lse, ws, ws_bytes, None)
+
+
+def bwd(L, p, q=Q, k=K, v=V, o=O, do=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, ws=WS, ws_bytes=1 << 30):
+    return L.attn_bwd(ctypes.byref(p), q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, None)
+
+
+def expect(L, status, want, fragment):
+    assert status == want, (B.STATUS.get(status), L.attn_last_error())
+    assert fragment in L.attn_last_error().decode()
+
+
+def test_null_problem(L):
+    expect(L, fwd(L, None), INVALID, "NULL")
+
+
+@pytest.mark.parametrize("field,value,want,frag", [
+    ("abi_version", 2, UNSUPPORTED, "abi_version"),
+    ("dtype", 7, UNSUPPORTED, "dtype"),
+    ("mask", 3, UNSUPPORTED, "mask"),
+    ("mask", -1, UNSUPPORTED, "mask"),
+    ("head_dim", 96, UNSUPPORTED, "head_dim 96"),
+    ("head_dim", 0, INVALID, "head_dim"),
+    ("heads_q", 3, INVALID, "multiple"),
+    ("heads_kv", 0, INVALID, "head counts"),
+    ("batch", -1, INVALID, "batch"),
+    ("scale", float("inf"), INVALID, "scale"),
+    ("scale", float("nan"), INVALID, "scale"),
+    ("max_seqlen_q", -5, INVALID, "max_seqlen"),
+])
+def test_declines_bad_fields(L, field, value, want, frag):
+    p = dense_problem()
+    setattr(p, field, value)
+    expect(L, fwd(L, p), want, frag)
+    expect(L, bwd(L, p), want, frag)
+
+
+def test_declines_half_packed(L):
+    p = dense_problem()
+    p.cu_seqlens_q = 0x7000_0000
+    expect(L, fwd(L, p), INVALID, "both")
+
+
+@pytest.mark.parametrize("which", ["q_stride", "k_stride", "v_stride", "o_stride"])
+def test_stride_alignment(L, which):
+    p = dense_problem()
+    getattr(p, which)[1] = 132  # not a multiple of 8 elements
+    expect(L, fwd(L, p), ALIGN, which)
+    p = dense_problem()
+    getattr(p, which)[0] = -8
+    expect(L, fwd(L, p), INVALID, "negative")
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o"])
+def test_pointer_alignment_and_null(L, arg):
+    p = dense_problem()
+    kw = {arg: {"q": Q, "k": K, "v": V, "o": O}[arg] + 8}
+    expect(L, fwd(L, p, **kw), ALIGN, arg)
+    expect(L, fwd(L, p, **{arg: None}), INVALID, f"{arg} is NULL")
+
+
+def test_lse_alignment_and_null(L):
+    p = dense_problem()
+    expect(L, fwd(L, p, lse=LSE + 2), ALIGN, "lse")
+    expect(L, fwd(L, p, lse=None), INVALID, "lse")
+
+
+def test_output_overlap(L):
+    p = dense_problem()
+    expect(L, fwd(L, p, o=Q + 4096), OVERLAP, "o overlaps")
+    expect(L, fwd(L, p, lse=O + 64), OVERLAP, "o overlaps lse")
+    expect(L, fwd(L, p, lse=K + 64), OVERLAP, "lse overlaps")
+    expect(L, bwd(L, p, dk=DQ + 1024), OVERLAP, "dq overlaps dk")
+    expect(L, bwd(L, p, dv=DO), OVERLAP, "dv overlaps")
+    expect(L, bwd(L, p, ws=DK), OVERLAP, "overlaps")
+
+
+def test_workspace_sizes(L):
+    p = dense_problem(b=2, sq=256, hq=4)
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(p)) == 0
+    nq = 2 * 256
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(p)) == 256 + 2 * ((nq * 4 * 4 + 255) // 256 * 256)
+    pk = packed_problem(tq=1000, hq=4)
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(pk)) == 256
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(pk)) == 256 + 2 * ((1000 * 4 * 4 + 255) // 256 * 256)
+    bad = dense_problem(d=96)
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_workspace_capacity_and_alignment(L):
+    pk = packed_problem()
+    expect(L, fwd(L, pk, ws_bytes=128), WORKSPACE, "workspace")
+    expect(L, fwd(L, pk, ws=WS + 64), WORKSPACE, "aligned")
+    p = dense_problem()
+    need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    expect(L, bwd(L, p, ws_bytes=need - 1), WORKSPACE, "required")
+    expect(L, bwd(L, p, ws=None), WORKSPACE, "NULL")
+
+
+def test_cu_seqlens_alignment(L):
+    pk = packed_problem()
+    pk.cu_seqlens_q = 0x7000_0002
+    expect(L, fwd(L, pk), ALIGN, "cu_seqlens")
+
+
+def test_empty_batch_is_a_no_op(L):
+    p = dense_problem(b=0)
+    assert fwd(L, p) == OK
+    assert bwd(L, p) == OK
+    p = dense_problem(sq=0, skv=0)
+    assert fwd(L, p) == OK
+
+
+def test_last_error_is_thread_local(L):
+    import threading
+    p = dense_problem(d=96)
+    fwd(L, p)
+    mine = L.attn_last_error().decode()
+    other = {}
+
+    def run():
+        q = dense_problem()
+        q.mask = 9
+        fwd(L, q)
+        other["msg"] = L.attn_last_error().decode()
+
+    t = threading.Thread(target=run)
+    t.start()
+    t.join()
+    assert "head_dim" in mine and "mask" in other["msg"]
+    assert L.attn_last_error().decode() == mine
+
+
+def test_binding_rejects_host_tensors(lib_path):
+    import torch
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        B.attn_fwd(q, q, q)
+
+
+def test_problem_struct_layout():
+    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3]
+    assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24
+    assert B.AttnProblem.cu_seqlens_q.offset == 40
+    assert B.AttnProblem.q_stride.offset == 72

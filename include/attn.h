@@ -82,7 +82,7 @@ typedef struct attn_problem {
   int32_t abi_version; /* must be ATTN_ABI_VERSION                                   */
   int32_t dtype;       /* attn_dtype_t: element type of Q, K, V, O, dO, dQ, dK, dV    */
   int32_t mask;        /* attn_mask_t                                                 */
-  float scale;         /* multiplies Q K^T before masking and softmax (1/sqrt(D) usually) */
+  float scale;         /* > 0; multiplies Q K^T before masking and softmax (1/sqrt(D) usually) */
   int32_t batch;       /* dense batch size or number of packed sequences (>= 0)       */
   int32_t heads_q;     /* Hq >= 1                                                     */
   int32_t heads_kv;    /* Hkv >= 1, Hq % Hkv == 0                                     */

@@ -83,6 +83,7 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256 && p->head_dim != 512)
     return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not built (64, 128, 256, 512)", p->head_dim);
   if (!isfinite(p->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
+  if (!(p->scale > 0.f)) return fail(ATTN_E_UNSUPPORTED, "scale %g is not positive", (double)p->scale);
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
   const bool packed = p->cu_seqlens_q != nullptr;
   if (packed != (p->cu_seqlens_kv != nullptr))

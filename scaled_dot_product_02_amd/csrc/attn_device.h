@@ -112,4 +112,32 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Reductions over the lane pair (l, l ^ 32) with v_permlane32_swap (no LDS round trip): the swap
+// of x with itself leaves x[l % 32] in the first and x[32 + l % 32] in the second result.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// True on every lane if the predicate holds on any lane of the wave (wave-uniform branch).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Workgroup order. The hardware hands workgroup i of a 1-D grid to XCD i % 8, each XCD with its own
+// L2. Map the n = units * tiles workgroups so that each XCD receives a contiguous run of
+// (unit, tile) pairs, unit-major: the workgroups in flight on an XCD then share one unit's K/V (or
+// Q/dO) stream in that XCD's L2. Within a unit, tiles run in the given order (longest first for
+// causal masks). Falls back to the plain order when n is not a multiple of 8.
+__device__ __forceinline__ void xcd_order(int units, int tiles, bool reverse, int& unit, int& tile) {
+  const int n = units * tiles;
+  const int i = blockIdx.x;
+  const int v = (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
+  unit = v / tiles;
+  tile = v % tiles;
+  if (reverse) tile = tiles - 1 - tile;
+}
+
 }  // namespace sdpa

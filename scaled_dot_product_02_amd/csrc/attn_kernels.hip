@@ -114,12 +114,21 @@ __global__ void __launch_bounds__(256) validate_cu_kernel(AttnShape s) {
 // Forward. Workgroup = 4 waves = 128 query rows of one (sequence, q-head); wave w owns rows
 // q0 + 32w .. +31. Per key tile of BN keys the wave computes S^T = K Q^T with 32x32x16 MFMAs
 // (A = K rows from LDS, B = its Q fragment held in VGPRs), so lane l holds query l%32 and half
-// of the tile's keys: the row max/sum need one cross-lane exchange (lanes l and l^32). The
-// accumulator layout of S^T is fed straight back as the B operand of O^T += V^T P^T (k slots
+// of the tile's keys: the row max/sum need one exchange between lanes l and l^32 (permlane swap).
+// The accumulator layout of S^T is fed straight back as the B operand of O^T += V^T P^T (k slots
 // permuted consistently), with V^T fetched by transpose reads.
+//
+// Softmax in the log2 domain with a lazy reference: P = exp2(S*c - m_ref) where m_ref is the
+// row's scaled running max at the last rescale; the O accumulator and row sum are rescaled only
+// when some row's max has grown by more than 2^8 since (wave-uniform branch), so P <= 2^8.
+// This is exact in real arithmetic (the reference cancels in O / l and LSE = m_ref + log2 l).
+// MINW = minimum waves per SIMD requested from the compiler (2 lets two workgroups share a CU so
+// one wave's softmax overlaps another's MFMAs).
 // ------------------------------------------------------------------------------------------
-template <int D, int BN, typename T>
-__global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D, int BN, int MINW, typename T>
+__global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
   constexpr int CH = D / 8;
   constexpr int TILE = BN * D;               // 16-bit elements of one K or V tile
@@ -136,8 +145,9 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
   }
   const int lane = threadIdx.x & 63, w = wave_id();
   const int hh = lane >> 5, lrow = lane & 31;
-  const int b = blockIdx.x / s.hq, h = blockIdx.x % s.hq, g = h / s.group;
-  const int qt = s.mask != 0 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  int bh, qt;
+  xcd_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, bh, qt);
+  const int b = bh / s.hq, h = bh % s.hq, g = h / s.group;
   const Seq sq = seq_info(s, b);
   const int q0 = qt * BM;
   if (q0 >= sq.sq) return;
@@ -150,6 +160,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
   const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
   const int qw0 = q0 + 32 * w;
   const int qi = qw0 + lrow;
+  const float c = s.scale_log2;
 
   v8s qf[D / 16];
   {
@@ -160,7 +171,8 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
   v16f oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = v16f{};
-  float m_run = -__builtin_inff(), l_run = 0.f;
+  float m_ref = -__builtin_inff();  // scaled (log2-domain) reference of this row
+  float l_run = 0.f;                // this lane's half of the row sum, relative to m_ref
 
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * TILE;
@@ -171,14 +183,14 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int c = (L % CH) ^ (r & 7);
+      const int cc = (L % CH) ^ (r & 7);
       const int64_t kr = min(kv0 + r, sq.skv - 1);
-      dma16(kg + kr * a.ak.row + c * 8, ks + slot * 8);
-      dma16(vg + kr * a.av.row + c * 8, vs + slot * 8);
+      dma16(kg + kr * a.ak.row + cc * 8, ks + slot * 8);
+      dma16(vg + kr * a.av.row + cc * 8, vs + slot * 8);
     }
   };
 
-  const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+  const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
   if (n_tiles > 0) issue(0, 0);
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
@@ -201,42 +213,44 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
         sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
       }
     }
-    // online softmax, log2 domain; this lane's query is qi, its keys kv0 + 32kb + 8(jr/4) + 4hh + jr%4
+    // row max of the raw scores (scale c > 0); this lane's keys are kv0 + 32kb + 8(jr/4) + 4hh + jr%4
     float mt = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int jr = 0; jr < 16; ++jr) {
-        float x = sacc[kb][jr] * s.scale_log2;
+        float x = sacc[kb][jr];
         if (need_mask) {
           const int key = kv0 + 32 * kb + 8 * (jr >> 2) + 4 * hh + (jr & 3);
           const bool ok = key < sq.skv && (s.mask == 0 || key <= qi + delta);
           x = ok ? x : -__builtin_inff();
+          sacc[kb][jr] = x;
         }
-        sacc[kb][jr] = x;
         mt = fmaxf(mt, x);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
+    const float m_new = pair32_max(mt) * c;
+    if (wave_any(m_new > m_ref + kRescaleThreshold)) {
+      const float ref = fmaxf(m_ref, m_new);
+      // 0 when m_ref = -inf; rows still without any key keep ref = -inf (O and l are 0 there)
+      const float alpha = ref == -__builtin_inff() ? 0.f : fast_exp2(m_ref - ref);
+      m_ref = ref;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
+    }
+    const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;  // rows with no key yet: every P is 0
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int jr = 0; jr < 16; ++jr) {
-        const float p = fast_exp2(sacc[kb][jr] - m_use);
+        const float p = fast_exp2(__builtin_fmaf(sacc[kb][jr], c, -m_use));
         sacc[kb][jr] = p;
-        rs += p;
+        l_run += p;
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     // O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
-    for (int c = 0; c < BN / 16; ++c) {
-      const int kb = c >> 1, half = c & 1;
+    for (int cb = 0; cb < BN / 16; ++cb) {
+      const int kb = cb >> 1, half = cb & 1;
       const auto pb = pack8<T>(sacc[kb][8 * half + 0], sacc[kb][8 * half + 1], sacc[kb][8 * half + 2],
                                sacc[kb][8 * half + 3], sacc[kb][8 * half + 4], sacc[kb][8 * half + 5],
                                sacc[kb][8 * half + 6], sacc[kb][8 * half + 7]);
@@ -244,7 +258,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
       const int row2 = row1 + 8;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int col = 32 * dt + 16 * (G & 1) + 4 * cc;
+        const int col = 32 * dt + 16 * (G & 1) + 4 * c4;
         const int chunk = col >> 3, within = col & 7;
         const v4s lo = lds_read_tr(vs, row1 * D + ((chunk ^ (row1 & 7)) << 3) + within);
         const v4s hi = lds_read_tr(vs, row2 * D + ((chunk ^ (row2 & 7)) << 3) + within);
@@ -253,7 +267,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
     }
   }
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = pair32_sum(l_run);
   if (qi < sq.sq) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     T* op = (T*)a.o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head + (int64_t)qi * a.ao.row;
@@ -270,7 +284,7 @@ __global__ void __launch_bounds__(256) attn_fwd_kernel(FwdArgs a) {
       }
     if (hh == 0) {
       float* lp = a.lse + seq_off(a.alse, packed, b, sq.tq0) + (int64_t)h * a.alse.head + (int64_t)qi * a.alse.row;
-      *lp = lt > 0.f ? (m_run + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+      *lp = lt > 0.f ? (m_ref + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
     }
   }
 }
@@ -663,10 +677,12 @@ int launch_validate_cu(const AttnShape& s, void* stream) {
   return (int)hipGetLastError();
 }
 
+template <int D> constexpr int fwd_minw() { return D <= 128 ? 2 : 1; }
+
 template <int D, typename T>
 static int fwd_t(const FwdArgs& a, hipStream_t st) {
-  const dim3 grid(a.s.batch * a.s.hq, a.s.n_qtiles);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), T>), grid, dim3(256), 0, st, a);
+  const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 

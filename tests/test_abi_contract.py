@@ -104,6 +104,8 @@ def test_null_problem(L):
     ("batch", -1, INVALID, "batch"),
     ("scale", float("inf"), INVALID, "scale"),
     ("scale", float("nan"), INVALID, "scale"),
+    ("scale", 0.0, UNSUPPORTED, "not positive"),
+    ("scale", -0.125, UNSUPPORTED, "not positive"),
     ("max_seqlen_q", -5, INVALID, "max_seqlen"),
 ])
 def test_declines_bad_fields(L, field, value, want, frag):

@@ -342,8 +342,8 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
 //   dV += P^T dO, dK += dS^T Q  (A = the P / dS accumulators as they are, B = dO / Q by transpose
 //   reads). dK is scaled once at the end; keys no query sees get exact zeros.
 // ------------------------------------------------------------------------------------------
-template <int D, int KB, typename T>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
+template <int D, int KB, int MINW, typename T>
+__global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = 4, KW = 16 * KB, BKV = NW * KW, BQ = 32, CH = D / 8;
   constexpr int QTILE = BQ * D;
   constexpr int NDMA = QTILE * 2 / 1024 / NW;
@@ -519,8 +519,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_kernel(BwdArgs a) {
 //   P = exp2(S*c - lse2), dS = P (dP - D)            (lse2, D are per-lane scalars)
 //   dQ += dS K                  (A = the dS accumulators, B = K by transpose reads)
 // ------------------------------------------------------------------------------------------
-template <int D, int QB, typename T>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a) {
+template <int D, int QB, int MINW, typename T>
+__global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NW = 4, QW = 16 * QB, BMQ = NW * QW, BK = 32, CH = D / 8;
   constexpr int KTILE = BK * D;
   constexpr int NDMA = KTILE * 2 / 1024 / NW;
@@ -667,6 +667,7 @@ constexpr int kFwdBM = 128;
 template <int D> constexpr int fwd_bn() { return D <= 256 ? 64 : 32; }
 template <int D> constexpr int dkdv_kb() { return D <= 256 ? 2 : 1; }
 template <int D> constexpr int dq_qb() { return D <= 256 ? 2 : 1; }
+template <int D> constexpr int bwd_minw() { return D <= 128 ? 2 : 1; }
 
 int fwd_query_tile(int) { return kFwdBM; }
 int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 256 ? 2 : 1); }
@@ -697,12 +698,12 @@ static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((passes & kPassDkdv) && a.n_kvtiles > 0) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), T>), dim3(a.s.batch * a.s.hkv, a.n_kvtiles),
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), bwd_minw<D>(), T>), dim3(a.s.batch * a.s.hkv, a.n_kvtiles),
                        dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((passes & kPassDq) && a.s.n_qtiles > 0) {
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), T>), dim3(a.s.batch * a.s.hq, a.s.n_qtiles), dim3(256),
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T>), dim3(a.s.batch * a.s.hq, a.s.n_qtiles), dim3(256),
                        0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }

@@ -107,6 +107,10 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // Swizzled position of 16-byte chunk c of row r in an LDS tile with `chunks` chunks per row:
 // XOR with the row's low 3 bits spreads 8 consecutive rows over 8 distinct bank groups.
 __device__ __forceinline__ int swz(int r, int c, int chunks) { return r * chunks * 8 + ((c ^ (r & 7)) << 3); }
+// The XOR only touches the low 3 bits of the chunk index, so an address splits into a per-lane
+// base for the chunk's low bits (few distinct values) plus a compile-time offset for its high bits
+// and for whole rows that are multiples of 8: swz(r + 8m, c) = swz_lo(r, c & 7, D) + 8m*D + 8*(c & ~7).
+__device__ __forceinline__ int swz_lo(int r, int c_lo, int d) { return r * d + ((c_lo ^ (r & 7)) << 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

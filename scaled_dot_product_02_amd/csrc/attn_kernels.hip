@@ -191,6 +191,15 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   };
 
   const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
+  // LDS read offsets: per-lane bases for the swizzled low chunk bits, the rest is compile-time.
+  // K rows (A of S^T): row 32kb + lrow, chunk 2kk + hh  -> koff[kk & 3] + 32kb*D + 64*(kk >> 2)
+  // V^T (transpose reads): row 32kb + 16half + 4hh + rr (+8), chunk 4dt + 2(G&1) + c4/2
+  //                        -> voff[dt & 1] + (32kb + 16half)*D + 64*(dt >> 1)
+  int koff[4], voff[2];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) koff[e] = swz_lo(lrow, 2 * e + hh, D);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) voff[e] = swz_lo(4 * hh + rr, 4 * e + 2 * (G & 1) + (c4 >> 1), D) + 4 * (c4 & 1);
   if (n_tiles > 0) issue(0, 0);
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
@@ -206,10 +215,9 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       sacc[kb] = v16f{};
-      const int r = 32 * kb + lrow;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const v8s kf = lds_read16(ks, swz(r, 2 * kk + hh, CH));
+        const v8s kf = lds_read16(ks, koff[kk & 3] + 32 * kb * D + 64 * (kk >> 2));
         sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
       }
     }
@@ -254,14 +262,11 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
       const auto pb = pack8<T>(sacc[kb][8 * half + 0], sacc[kb][8 * half + 1], sacc[kb][8 * half + 2],
                                sacc[kb][8 * half + 3], sacc[kb][8 * half + 4], sacc[kb][8 * half + 5],
                                sacc[kb][8 * half + 6], sacc[kb][8 * half + 7]);
-      const int row1 = 32 * kb + 16 * half + 4 * (G >> 1) + rr;
-      const int row2 = row1 + 8;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int col = 32 * dt + 16 * (G & 1) + 4 * c4;
-        const int chunk = col >> 3, within = col & 7;
-        const v4s lo = lds_read_tr(vs, row1 * D + ((chunk ^ (row1 & 7)) << 3) + within);
-        const v4s hi = lds_read_tr(vs, row2 * D + ((chunk ^ (row2 & 7)) << 3) + within);
+        const int o1 = voff[dt & 1] + (32 * kb + 16 * half) * D + 64 * (dt >> 1);
+        const v4s lo = lds_read_tr(vs, o1);
+        const v4s hi = lds_read_tr(vs, o1 + 8 * D);
         oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
       }
     }
@@ -283,6 +288,193 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
         *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
       }
     if (hh == 0) {
+      float* lp = a.lse + seq_off(a.alse, packed, b, sq.tq0) + (int64_t)h * a.alse.head + (int64_t)qi * a.alse.row;
+      *lp = lt > 0.f ? (m_ref + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Forward for large head dims (D = 256, 512). A 32-row query block with all of its D in one wave
+// needs Q (D/4 registers) plus the O accumulator (D/2) — more than the 256 registers that keep two
+// waves per SIMD. So each 32-row block is shared by a wave pair: wave w (w < 4) and w + 4 own
+// rows q0 + 32*(w&3) .. +31, and wave half hf = w/4 owns head-dim columns [hf*D/2, (hf+1)*D/2).
+// Per key tile (BN = 32 keys) each wave computes the partial S^T over its half of D, the pair
+// swaps partials through LDS (fp32) and adds own + partner (commutative: both waves hold the same
+// bits), then both run the identical softmax and each accumulates O^T for its half of D. Every
+// wave executes every barrier; a wave pair with no allowed key in a tile skips only its MFMAs.
+// ------------------------------------------------------------------------------------------
+template <int D, typename T>
+__global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
+  constexpr int BM = 128, BN = 32, NW = 8, DH = D / 2;
+  constexpr int CH = D / 8;
+  constexpr int TILE = BN * D;
+  constexpr int NDMA = TILE * 2 / 1024 / NW;
+  static_assert(NDMA >= 1 && (TILE * 2) % (1024 * NW) == 0, "tile must split evenly over 8 waves");
+  __shared__ __attribute__((aligned(1024))) us smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float xch[NW * 16 * 64];  // partial S^T per wave
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<D, T>(a.o, a.ao, s.total_q, s.hq);
+    for (int64_t i = flat_block() * blockDim.x + threadIdx.x; i < s.total_q * s.hq; i += flat_grid_threads())
+      a.lse[(i / s.hq) * a.alse.row + (i % s.hq) * a.alse.head] = __builtin_nanf("");
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int pw = w & 3, hf = w >> 2;
+  const int hh = lane >> 5, lrow = lane & 31;
+  int bh, qt;
+  xcd_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, bh, qt);
+  const int b = bh / s.hq, h = bh % s.hq, g = h / s.group;
+  const Seq sq = seq_info(s, b);
+  const int q0 = qt * BM;
+  if (q0 >= sq.sq) return;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BM + delta) : sq.skv;
+  const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  const us* qg = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  const int qw0 = q0 + 32 * pw;
+  const int qi = qw0 + lrow;
+  const float c = s.scale_log2;
+
+  v8s qf[DH / 16];  // this wave's half of the row: d = hf*DH + 16kk + 8hh + t
+  {
+    const us* p = qg + (int64_t)min(qi, sq.sq - 1) * a.aq.row + hf * DH + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = *reinterpret_cast<const v8s*>(p + 16 * kk);
+  }
+  v16f oacc[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt) oacc[dt] = v16f{};
+  float m_ref = -__builtin_inff();
+  float l_run = 0.f;
+
+  auto issue = [&](int tile, int stage) {
+    us* ks = smem + stage * 2 * TILE;
+    us* vs = ks + TILE;
+    const int kv0 = tile * BN;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot = (w * NDMA + i) * 64;
+      const int L = slot + lane;
+      const int r = L / CH;
+      const int cc = (L % CH) ^ (r & 7);
+      const int64_t kr = min(kv0 + r, sq.skv - 1);
+      dma16(kg + kr * a.ak.row + cc * 8, ks + slot * 8);
+      dma16(vg + kr * a.av.row + cc * 8, vs + slot * 8);
+    }
+  };
+
+  float* mine = xch + w * 1024;
+  const float* other = xch + (w ^ 4) * 1024;
+  const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
+  // same offset scheme as the D <= 128 forward, shifted by this wave's half of D
+  int koff[4], voff[2];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) koff[e] = swz_lo(lrow, 2 * e + hh, D) + hf * DH;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    voff[e] = swz_lo(4 * hh + rr, 4 * e + 2 * (G & 1) + (c4 >> 1), D) + 4 * (c4 & 1) + hf * DH;
+  if (n_tiles > 0) issue(0, 0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    const us* ks = smem + (j & 1) * 2 * TILE;
+    const us* vs = ks + TILE;
+    const int kv0 = j * BN;
+    const bool active = s.mask == 0 || kv0 <= qw0 + 31 + delta;  // same for both waves of a pair
+    v16f sacc = v16f{};
+    if (active) {
+#pragma unroll
+      for (int kk = 0; kk < DH / 16; ++kk) {
+        const v8s kf = lds_read16(ks, koff[kk & 3] + 64 * (kk >> 2));
+        sacc = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {  // 4 floats per lane per group: conflict-free 16-byte writes
+        v4f t4 = {sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
+        *reinterpret_cast<v4f*>(mine + (q4 * 64 + lane) * 4) = t4;
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const v4f t4 = *reinterpret_cast<const v4f*>(other + (q4 * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] += t4[i];
+    }
+    const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta);
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int jr = 0; jr < 16; ++jr) {
+      float x = sacc[jr];
+      if (need_mask) {
+        const int key = kv0 + 8 * (jr >> 2) + 4 * hh + (jr & 3);
+        const bool ok = key < sq.skv && (s.mask == 0 || key <= qi + delta);
+        x = ok ? x : -__builtin_inff();
+        sacc[jr] = x;
+      }
+      mt = fmaxf(mt, x);
+    }
+    const float m_new = pair32_max(mt) * c;
+    {  // branch-free form of the lazy rescale (alpha = 1 unless some row of the wave needs it)
+      const bool need = wave_any(m_new > m_ref + kRescaleThreshold);
+      const float ref = need ? fmaxf(m_ref, m_new) : m_ref;
+      const float alpha = (!need || ref == -__builtin_inff()) ? (need ? 0.f : 1.f) : fast_exp2(m_ref - ref);
+      m_ref = ref;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) oacc[dt] *= alpha;
+    }
+    const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
+#pragma unroll
+    for (int jr = 0; jr < 16; ++jr) {
+      const float p = fast_exp2(__builtin_fmaf(sacc[jr], c, -m_use));
+      sacc[jr] = p;
+      l_run += p;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const auto pb = pack8<T>(sacc[8 * half + 0], sacc[8 * half + 1], sacc[8 * half + 2], sacc[8 * half + 3],
+                               sacc[8 * half + 4], sacc[8 * half + 5], sacc[8 * half + 6], sacc[8 * half + 7]);
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) {
+        const int o1 = voff[dt & 1] + 16 * half * D + 64 * (dt >> 1);
+        const v4s lo = lds_read_tr(vs, o1);
+        const v4s hi = lds_read_tr(vs, o1 + 8 * D);
+        oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
+      }
+      // bound the transpose reads in flight (register pressure): 2 reads per MFMA, in order
+#pragma unroll
+      for (int dt = 0; dt < DH / 32; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+  }
+
+  const float lt = pair32_sum(l_run);
+  if (qi < sq.sq) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    T* op = (T*)a.o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head + (int64_t)qi * a.ao.row + hf * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        typename Elem<T>::op4 v;
+        v[0] = Elem<T>::cvt(oacc[dt][4 * q4 + 0] * inv);
+        v[1] = Elem<T>::cvt(oacc[dt][4 * q4 + 1] * inv);
+        v[2] = Elem<T>::cvt(oacc[dt][4 * q4 + 2] * inv);
+        v[3] = Elem<T>::cvt(oacc[dt][4 * q4 + 3] * inv);
+        *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
+      }
+    if (hh == 0 && hf == 0) {
       float* lp = a.lse + seq_off(a.alse, packed, b, sq.tq0) + (int64_t)h * a.alse.head + (int64_t)qi * a.alse.row;
       *lp = lt > 0.f ? (m_ref + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
     }
@@ -417,6 +609,13 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     if (w == 1) dma4(a.rowsum + row, rss);
   };
 
+  // LDS read offsets (see swz_lo): Q/dO rows 16qb + l16, chunk 4kk + G -> roff[kk & 1] + 16qb*D + 64*(kk >> 1);
+  // transpose reads: rows 4G + rr (+16), chunk 2dt + c4/2 -> toff[dt & 3] + 64*(dt >> 2)
+  int roff[2], toff[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1);
   if (n_it > 0) issue(0, 0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
@@ -439,11 +638,11 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
         sv[qb][kb] = v4f{};
         dp[qb][kb] = v4f{};
       }
-      const int r = 16 * qb + l16;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const v8s qa = lds_read16(qs, swz(r, 4 * kk + G, CH));
-        const v8s da = lds_read16(dos, swz(r, 4 * kk + G, CH));
+        const int o = roff[kk & 1] + 16 * qb * D + 64 * (kk >> 1);
+        const v8s qa = lds_read16(qs, o);
+        const v8s da = lds_read16(dos, o);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           sv[qb][kb] = Elem<T>::mma16(Elem<T>::cast(qa), Elem<T>::cast(kf[kb][kk]), sv[qb][kb]);
@@ -478,13 +677,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       sa[kb] = pack8<T>(dp[0][kb][0], dp[0][kb][1], dp[0][kb][2], dp[0][kb][3], dp[1][kb][0], dp[1][kb][1],
                         dp[1][kb][2], dp[1][kb][3]);
     }
-    const int row1 = 4 * G + rr, row2 = row1 + 16;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int col = 16 * dt + 4 * cc;
-      const int chunk = col >> 3, within = col & 7;
-      const int o1 = row1 * D + ((chunk ^ (row1 & 7)) << 3) + within;
-      const int o2 = row2 * D + ((chunk ^ (row2 & 7)) << 3) + within;
+      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const int o2 = o1 + 16 * D;
       const v8s dob = cat44(lds_read_tr(dos, o1), lds_read_tr(dos, o2));
       const v8s qbt = cat44(lds_read_tr(qs, o1), lds_read_tr(qs, o2));
 #pragma unroll
@@ -584,6 +780,12 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
+  // LDS read offsets as in the dK/dV pass: K/V rows 16kb + l16 -> roff; K transpose reads -> toff
+  int roff[2], toff[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1);
   if (n_tiles > 0) issue(0, 0);
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
@@ -603,11 +805,11 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
         st[kb][qb] = v4f{};
         dpt[kb][qb] = v4f{};
       }
-      const int r = 16 * kb + l16;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const v8s ka = lds_read16(ks, swz(r, 4 * kk + G, CH));
-        const v8s va = lds_read16(vs, swz(r, 4 * kk + G, CH));
+        const int o = roff[kk & 1] + 16 * kb * D + 64 * (kk >> 1);
+        const v8s ka = lds_read16(ks, o);
+        const v8s va = lds_read16(vs, o);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           st[kb][qb] = Elem<T>::mma16(Elem<T>::cast(ka), Elem<T>::cast(qf[qb][kk]), st[kb][qb]);
@@ -634,13 +836,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
         }
       dsa[qb] = pack8<T>(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
     }
-    const int row1 = 4 * G + rr, row2 = row1 + 16;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int col = 16 * dt + 4 * cc;
-      const int chunk = col >> 3, within = col & 7;
-      const v8s kbt = cat44(lds_read_tr(ks, row1 * D + ((chunk ^ (row1 & 7)) << 3) + within),
-                            lds_read_tr(ks, row2 * D + ((chunk ^ (row2 & 7)) << 3) + within));
+      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const v8s kbt = cat44(lds_read_tr(ks, o1), lds_read_tr(ks, o1 + 16 * D));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) dq[qb][dt] = Elem<T>::mma16(dsa[qb], Elem<T>::cast(kbt), dq[qb][dt]);
     }
@@ -664,26 +863,30 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 // Launchers
 // ------------------------------------------------------------------------------------------
 constexpr int kFwdBM = 128;
-template <int D> constexpr int fwd_bn() { return D <= 256 ? 64 : 32; }
-template <int D> constexpr int dkdv_kb() { return D <= 256 ? 2 : 1; }
-template <int D> constexpr int dq_qb() { return D <= 256 ? 2 : 1; }
-template <int D> constexpr int bwd_minw() { return D <= 128 ? 2 : 1; }
+template <int D> constexpr int fwd_bn() { return D <= 128 ? 64 : 32; }
+template <int D> constexpr int dkdv_kb() { return D <= 128 ? 2 : 1; }
+template <int D> constexpr int dq_qb() { return D <= 128 ? 2 : 1; }
+template <int D> constexpr int bwd_minw() { return D <= 256 ? 2 : 1; }
 
 int fwd_query_tile(int) { return kFwdBM; }
-int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 256 ? 2 : 1); }
-int bwd_query_tile(int head_dim) { return 64 * (head_dim <= 256 ? 2 : 1); }
+int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }
+int bwd_query_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }
 
 int launch_validate_cu(const AttnShape& s, void* stream) {
   hipLaunchKernelGGL(validate_cu_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, s);
   return (int)hipGetLastError();
 }
 
-template <int D> constexpr int fwd_minw() { return D <= 128 ? 2 : 1; }
+template <int D> constexpr int fwd_minw() { return D <= 256 ? 2 : 1; }
 
 template <int D, typename T>
 static int fwd_t(const FwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+  if constexpr (D <= 128) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_split_kernel<D, T>), grid, dim3(512), 0, st, a);
+  }
   return (int)hipGetLastError();
 }
 

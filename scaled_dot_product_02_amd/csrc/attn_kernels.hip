@@ -145,9 +145,10 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   }
   const int lane = threadIdx.x & 63, w = wave_id();
   const int hh = lane >> 5, lrow = lane & 31;
-  int bh, qt;
-  xcd_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, bh, qt);
-  const int b = bh / s.hq, h = bh % s.hq, g = h / s.group;
+  int u, qt, b, h;
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt);
+  q_unit(u, s.batch, s.hkv, s.group, b, h);
+  const int g = h / s.group;
   const Seq sq = seq_info(s, b);
   const int q0 = qt * BM;
   if (q0 >= sq.sq) return;
@@ -324,9 +325,10 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int pw = w & 3, hf = w >> 2;
   const int hh = lane >> 5, lrow = lane & 31;
-  int bh, qt;
-  xcd_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, bh, qt);
-  const int b = bh / s.hq, h = bh % s.hq, g = h / s.group;
+  int u, qt, b, h;
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt);
+  q_unit(u, s.batch, s.hkv, s.group, b, h);
+  const int g = h / s.group;
   const Seq sq = seq_info(s, b);
   const int q0 = qt * BM;
   if (q0 >= sq.sq) return;
@@ -551,9 +553,11 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   }
   const int lane = threadIdx.x & 63, w = wave_id();
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
-  const int b = blockIdx.x / s.hkv, g = blockIdx.x % s.hkv;
+  int u, kt;
+  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
+  const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
-  const int k0 = blockIdx.y * BKV;
+  const int k0 = kt * BKV;
   if (k0 >= sq.skv) return;
   const int kw0 = k0 + w * KW;
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
@@ -730,8 +734,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   }
   const int lane = threadIdx.x & 63, w = wave_id();
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
-  const int b = blockIdx.x / s.hq, h = blockIdx.x % s.hq, g = h / s.group;
-  const int qt = s.mask != 0 ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  int u, qt, b, h;
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt);
+  q_unit(u, s.batch, s.hkv, s.group, b, h);
+  const int g = h / s.group;
   const Seq sq = seq_info(s, b);
   const int q0 = qt * BMQ;
   if (q0 >= sq.sq) return;
@@ -860,6 +866,318 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Backward for D = 512. One wave cannot hold 16 keys' K and V fragments (128 registers) plus their
+// dK and dV accumulators (256), nor 16 query rows' Q and dO (128) plus dQ (128), within the 256
+// registers that keep two waves per SIMD. So both passes pair waves (8 waves per workgroup):
+//
+// dK/dV: the pair (w, w+4) owns 16 keys. Wave w holds K, computes S = Q K^T and P = exp2(S*c - lse2),
+// hands P (fp32) to its partner through LDS and accumulates dV += P^T dO. Wave w+4 holds V, computes
+// dP = dO V^T, takes P, forms dS = P (dP - D) and accumulates dK += dS^T Q. Both do 4*D MFMA work
+// per pair. dQ: the pair owns 16 query rows; wave w holds Q and computes P, wave w+4 holds dO and
+// computes dP, they swap (fp32), both form the same dS, and each accumulates half of dQ's columns.
+// Every wave executes every barrier; a pair whose keys / rows see nothing in a tile skips its MFMAs.
+// ------------------------------------------------------------------------------------------
+template <int D, typename T>
+__global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
+  constexpr int NW = 8, KW = 16, BKV = 4 * KW, BQ = 32, CH = D / 8;
+  constexpr int QTILE = BQ * D;
+  constexpr int NDMA = QTILE * 2 / 1024 / NW;
+  static_assert(NDMA >= 1, "query tile must split over 8 waves");
+  constexpr int STAGE = 2 * QTILE + 2 * 64 * 2;  // Q, dO tiles, then lse2[64] and D[64] as floats
+  __shared__ __attribute__((aligned(1024))) us smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float xch[4 * 2 * 64 * 4];  // P per pair: [qb][lane][4]
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<D, T>(a.dk, a.ak, s.total_kv, s.hkv);
+    fill_nan_rows<D, T>(a.dv, a.av, s.total_kv, s.hkv);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int pr = w & 3, role = w >> 2;  // role 0: K, S, P, dV; role 1: V, dP, dS, dK
+  const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
+  int u, kt;
+  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
+  const int b = u / s.hkv, g = u % s.hkv;
+  const Seq sq = seq_info(s, b);
+  const int k0 = kt * BKV;
+  if (k0 >= sq.skv) return;
+  const int kw0 = k0 + pr * KW;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int q_lo = s.mask != 0 ? max(0, k0 - delta) : 0;
+  const int qt0 = q_lo / BQ;
+  const int nq = max(0, (sq.sq + BQ - 1) / BQ - qt0);
+  const int n_it = nq * s.group;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
+
+  // role 0 keeps K, role 1 keeps V (B operands: key kw0 + l16, d = 32kk + 8G + t)
+  const us* kvg = role == 0 ? (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head
+                            : (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  const int64_t kvrow = role == 0 ? a.ak.row : a.av.row;
+  v8s kvf[D / 32];
+  {
+    const int64_t r = min(kw0 + l16, sq.skv - 1);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) kvf[kk] = *reinterpret_cast<const v8s*>(kvg + r * kvrow + 32 * kk + 8 * G);
+  }
+  v4f acc[D / 16];  // dV (role 0) or dK (role 1): key kw0 + 4G + i, d = 16dt + l16
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = v4f{};
+
+  auto issue = [&](int it, int stage) {
+    const int hi = it / nq, qt = qt0 + it % nq;
+    const int h = g * s.group + hi;
+    const int qs0 = qt * BQ;
+    us* qs = smem + stage * STAGE;
+    us* dos = qs + QTILE;
+    float* l2s = reinterpret_cast<float*>(dos + QTILE);
+    float* rss = l2s + 64;
+    const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
+    const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot = (w * NDMA + i) * 64;
+      const int L = slot + lane;
+      const int r = L / CH;
+      const int c = (L % CH) ^ (r & 7);
+      const int64_t qr = min(qs0 + r, sq.sq - 1);
+      dma16(qgh + qr * a.aq.row + c * 8, qs + slot * 8);
+      dma16(dgh + qr * a.ao.row + c * 8, dos + slot * 8);
+    }
+    const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
+    if (w == 0) dma4(a.lse2 + row, l2s);
+    if (w == 1) dma4(a.rowsum + row, rss);
+  };
+
+  int roff[2], toff[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1);
+  float* pbuf = xch + pr * 2 * 64 * 4;
+
+  if (n_it > 0) issue(0, 0);
+  for (int it = 0; it < n_it; ++it) {
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < n_it) issue(it + 1, (it + 1) & 1);
+    const us* qs = smem + (it & 1) * STAGE;
+    const us* dos = qs + QTILE;
+    const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
+    const float* rss = l2s + 64;
+    const int qs0 = (qt0 + it % nq) * BQ;
+    const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0);
+    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1);
+    v4f sv[2];  // role 0: S then P; role 1: dP then dS
+    if (active) {
+      const us* src = role == 0 ? qs : dos;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sv[qb] = v4f{};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          sv[qb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, roff[kk & 1] + 16 * qb * D + 64 * (kk >> 1))),
+                                  Elem<T>::cast(kvf[kk]), sv[qb]);
+      }
+      if (role == 0) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const v4f l2 = *reinterpret_cast<const v4f*>(l2s + 16 * qb + 4 * G);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = fast_exp2(sv[qb][i] * s.scale_log2 - l2[i]);
+            if (need_mask) {
+              const int q = qs0 + 16 * qb + 4 * G + i;
+              const int key = kw0 + l16;
+              const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
+              p = ok ? p : 0.f;
+            }
+            sv[qb][i] = p;
+          }
+          *reinterpret_cast<v4f*>(pbuf + (qb * 64 + lane) * 4) = sv[qb];
+        }
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+    if (role == 1) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const v4f pv = *reinterpret_cast<const v4f*>(pbuf + (qb * 64 + lane) * 4);
+        const v4f dr = *reinterpret_cast<const v4f*>(rss + 16 * qb + 4 * G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[qb][i] = pv[i] * (sv[qb][i] - dr[i]);
+      }
+    }
+    const auto pa = pack8<T>(sv[0][0], sv[0][1], sv[0][2], sv[0][3], sv[1][0], sv[1][1], sv[1][2], sv[1][3]);
+    const us* bsrc = role == 0 ? dos : qs;  // dV += P^T dO ; dK += dS^T Q
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const v8s bt = cat44(lds_read_tr(bsrc, o1), lds_read_tr(bsrc, o1 + 16 * D));
+      acc[dt] = Elem<T>::mma16(pa, Elem<T>::cast(bt), acc[dt]);
+    }
+  }
+
+  T* outp = role == 0 ? (T*)a.dv + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head
+                      : (T*)a.dk + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const int64_t orow = role == 0 ? a.av.row : a.ak.row;
+  const float oscale = role == 0 ? 1.f : s.scale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = kw0 + 4 * G + i;
+    if (key < sq.skv) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) outp[(int64_t)key * orow + 16 * dt + l16] = Elem<T>::cvt(acc[dt][i] * oscale);
+    }
+  }
+}
+
+template <int D, typename T>
+__global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
+  constexpr int NW = 8, QW = 16, BMQ = 4 * QW, BK = 32, CH = D / 8, DH = D / 2;
+  constexpr int KTILE = BK * D;
+  constexpr int NDMA = KTILE * 2 / 1024 / NW;
+  static_assert(NDMA >= 1, "key tile must split over 8 waves");
+  __shared__ __attribute__((aligned(1024))) us smem[2 * 2 * KTILE];
+  __shared__ __attribute__((aligned(16))) float xch[NW * 2 * 64 * 4];  // P (role 0) / dP (role 1): [kb][lane][4]
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<D, T>(a.dq, a.aq, s.total_q, s.hq);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int pr = w & 3, role = w >> 2;  // role 0: Q, S, P; role 1: dO, dP. Role r accumulates dQ columns [r*DH, r*DH + DH)
+  const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
+  int u, qt, b, h;
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt);
+  q_unit(u, s.batch, s.hkv, s.group, b, h);
+  const int g = h / s.group;
+  const Seq sq = seq_info(s, b);
+  const int q0 = qt * BMQ;
+  if (q0 >= sq.sq) return;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BMQ + delta) : sq.skv;
+  const int n_tiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+  const int qw0 = q0 + pr * QW;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
+
+  const us* qdg = role == 0 ? (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head
+                            : (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+  const int64_t qdrow = role == 0 ? a.aq.row : a.ao.row;
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  v8s qdf[D / 32];
+  float l2, dr;
+  {
+    const int64_t r = min(qw0 + l16, sq.sq - 1);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qdf[kk] = *reinterpret_cast<const v8s*>(qdg + r * qdrow + 32 * kk + 8 * G);
+    l2 = a.lse2[(int64_t)h * a.nrows + rowbase + r];
+    dr = a.rowsum[(int64_t)h * a.nrows + rowbase + r];
+  }
+  v4f dq[DH / 16];  // rows qw0 + 4G + i, columns role*DH + 16dt + l16
+#pragma unroll
+  for (int dt = 0; dt < DH / 16; ++dt) dq[dt] = v4f{};
+
+  auto issue = [&](int tile, int stage) {
+    us* ks = smem + stage * 2 * KTILE;
+    us* vs = ks + KTILE;
+    const int kv0 = tile * BK;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int slot = (w * NDMA + i) * 64;
+      const int L = slot + lane;
+      const int r = L / CH;
+      const int c = (L % CH) ^ (r & 7);
+      const int64_t kr = min(kv0 + r, sq.skv - 1);
+      dma16(kg + kr * a.ak.row + c * 8, ks + slot * 8);
+      dma16(vg + kr * a.av.row + c * 8, vs + slot * 8);
+    }
+  };
+
+  int roff[2], toff[4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1) + role * DH;
+  float* mine = xch + w * 2 * 64 * 4;
+  const float* other = xch + (w ^ 4) * 2 * 64 * 4;
+
+  if (n_tiles > 0) issue(0, 0);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    const us* ks = smem + (j & 1) * 2 * KTILE;
+    const us* vs = ks + KTILE;
+    const int kv0 = j * BK;
+    const bool active = s.mask == 0 || kv0 <= qw0 + QW - 1 + delta;
+    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta);
+    v4f st[2];  // S^T -> P (role 0) or dP^T (role 1): key kv0 + 16kb + 4G + i, query qw0 + l16
+    if (active) {
+      const us* src = role == 0 ? ks : vs;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = v4f{};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+          st[kb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, roff[kk & 1] + 16 * kb * D + 64 * (kk >> 1))),
+                                  Elem<T>::cast(qdf[kk]), st[kb]);
+      }
+      if (role == 0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = fast_exp2(st[kb][i] * s.scale_log2 - l2);
+            if (need_mask) {
+              const int q = qw0 + l16;
+              const int key = kv0 + 16 * kb + 4 * G + i;
+              const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta);
+              p = ok ? p : 0.f;
+            }
+            st[kb][i] = p;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) *reinterpret_cast<v4f*>(mine + (kb * 64 + lane) * 4) = st[kb];
+    }
+    __syncthreads();
+    if (!active) continue;
+    float ds[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const v4f ot = *reinterpret_cast<const v4f*>(other + (kb * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = role == 0 ? st[kb][i] : ot[i];
+        const float dpv = role == 0 ? ot[i] : st[kb][i];
+        ds[kb][i] = p * (dpv - dr);
+      }
+    }
+    const auto dsa = pack8<T>(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const v8s kbt = cat44(lds_read_tr(ks, o1), lds_read_tr(ks, o1 + 16 * D));
+      dq[dt] = Elem<T>::mma16(dsa, Elem<T>::cast(kbt), dq[dt]);
+    }
+  }
+
+  T* dqp = (T*)a.dq + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head + role * DH;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = qw0 + 4 * G + i;
+    if (q < sq.sq) {
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[dt][i] * s.scale);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
 constexpr int kFwdBM = 128;
@@ -869,7 +1187,7 @@ template <int D> constexpr int dq_qb() { return D <= 128 ? 2 : 1; }
 template <int D> constexpr int bwd_minw() { return D <= 256 ? 2 : 1; }
 
 int fwd_query_tile(int) { return kFwdBM; }
-int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }
+int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }  // 64 for the D = 512 pair kernel too
 int bwd_query_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }
 
 int launch_validate_cu(const AttnShape& s, void* stream) {
@@ -901,13 +1219,21 @@ static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((passes & kPassDkdv) && a.n_kvtiles > 0) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), bwd_minw<D>(), T>), dim3(a.s.batch * a.s.hkv, a.n_kvtiles),
-                       dim3(256), 0, st, a);
+    const dim3 grid(a.s.batch * a.s.hkv * a.n_kvtiles);
+    if constexpr (D <= 256) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), bwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, T>), grid, dim3(512), 0, st, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((passes & kPassDq) && a.s.n_qtiles > 0) {
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T>), dim3(a.s.batch * a.s.hq, a.s.n_qtiles), dim3(256),
-                       0, st, a);
+    const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
+    if constexpr (D <= 256) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dq_pair_kernel<D, T>), grid, dim3(512), 0, st, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   return (int)e;

@@ -28,9 +28,27 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd+bwd TFLOP/s at D=128/512 bf16; % of MFMA bf16 peak"
 PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
-# Counter-derived HBM traffic per launch (KiB -> bytes, scaled by the copy-kernel factor) is
-# attached by hand only while the kernel is unchanged since the counters were taken; else null.
-TRAFFIC_BYTES = {}
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated against a plain device
+# copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
+# source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
+TRAFFIC = {
+    ("dense_d128", "bwd_dkdv"): {"src_sha1": "2bb7467cf3a3", "bytes": 855367009},
+    ("dense_d128", "fwd"): {"src_sha1": "2bb7467cf3a3", "bytes": 681779429},
+    ("dense_d128", "bwd_dq"): {"src_sha1": "2bb7467cf3a3", "bytes": 614351881},
+    ("dense_d128", "bwd_pre"): {"src_sha1": "2bb7467cf3a3", "bytes": 159446865},
+}
+
+
+def kernel_source_sha1():
+    import hashlib
+    path = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "attn_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()[:12]
+
+
+def traffic_for(workload, kernel):
+    t = TRAFFIC.get((workload, kernel))
+    return t["bytes"] if t and t["src_sha1"] == kernel_source_sha1() else None
 
 
 def log(*a):
@@ -149,7 +167,19 @@ def main():
     ap.add_argument("--workload", default="dense_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the informational D=512 line")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": n, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported (no multi-GPU path "
               "is built: sharding is described in the design notes, not implemented)", file=sys.stderr)
@@ -180,7 +210,7 @@ def main():
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_TFLOPS}
     roof["kernel"] = dom
     roof["avg_launch_ms"] = km[dom]
-    roof["traffic"] = TRAFFIC_BYTES.get((w.name, dom))
+    roof["traffic"] = traffic_for(w.name, dom)
     fwd_ms = km["fwd"]
     bwd_ms = km["bwd_pre"] + km["bwd_dkdv"] + km["bwd_dq"]
     out = {

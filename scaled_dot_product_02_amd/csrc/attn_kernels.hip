@@ -411,17 +411,14 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] += t4[i];
     }
-    const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta);
+    // Branch-free mask (a per-element branch here doubles the live S values and spills): key
+    // kv0 + 8(jr/4) + 4hh + jr%4 is allowed iff its offset 8(jr/4) + jr%4 <= lim - kv0 - 4hh.
+    const int lim = (s.mask != 0 ? min(sq.skv - 1, qi + delta) : sq.skv - 1) - kv0 - 4 * hh;
     float mt = -__builtin_inff();
 #pragma unroll
     for (int jr = 0; jr < 16; ++jr) {
-      float x = sacc[jr];
-      if (need_mask) {
-        const int key = kv0 + 8 * (jr >> 2) + 4 * hh + (jr & 3);
-        const bool ok = key < sq.skv && (s.mask == 0 || key <= qi + delta);
-        x = ok ? x : -__builtin_inff();
-        sacc[jr] = x;
-      }
+      const float x = (8 * (jr >> 2) + (jr & 3) <= lim) ? sacc[jr] : -__builtin_inff();
+      sacc[jr] = x;
       mt = fmaxf(mt, x);
     }
     const float m_new = pair32_max(mt) * c;

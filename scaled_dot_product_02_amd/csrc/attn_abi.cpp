@@ -104,6 +104,13 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
         return fail(ATTN_E_ALIGN, "%s_stride[%d] = %lld is not a multiple of 8 elements (16 bytes)", names[t], i,
                     (long long)strides[t][i]);
     }
+  // Tiles address rows with 32-bit offsets from a 64-bit tile base: (tile rows <= 128) x row stride
+  // must stay below 2^31 elements.
+  for (int t = 0; t < 4; ++t) {
+    const int64_t row = packed ? strides[t][0] : strides[t][1];
+    if (row >= (int64_t(1) << 24))
+      return fail(ATTN_E_UNSUPPORTED, "%s row stride %lld is not below 2^24 elements", names[t], (long long)row);
+  }
   info->packed = packed;
   info->nq = packed ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
   info->nkv = packed ? p->total_kv : (int64_t)p->batch * p->max_seqlen_kv;

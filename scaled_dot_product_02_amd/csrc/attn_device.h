@@ -104,13 +104,28 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
 // Wait until this wave's outstanding vector-memory loads (including LDS DMA) have landed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Swizzled position of 16-byte chunk c of row r in an LDS tile with `chunks` chunks per row:
-// XOR with the row's low 3 bits spreads 8 consecutive rows over 8 distinct bank groups.
-__device__ __forceinline__ int swz(int r, int c, int chunks) { return r * chunks * 8 + ((c ^ (r & 7)) << 3); }
-// The XOR only touches the low 3 bits of the chunk index, so an address splits into a per-lane
-// base for the chunk's low bits (few distinct values) plus a compile-time offset for its high bits
-// and for whole rows that are multiples of 8: swz(r + 8m, c) = swz_lo(r, c & 7, D) + 8m*D + 8*(c & ~7).
-__device__ __forceinline__ int swz_lo(int r, int c_lo, int d) { return r * d + ((c_lo ^ (r & 7)) << 3); }
+// LDS tile rows are stored with their 16-byte chunks permuted: physical chunk = logical chunk ^
+// sw_key(row). For D >= 128 (16+ chunks per row) the key is the row's low 4 bits, bit-permuted
+// (r0 r1 r2 r3 -> chunk bits 2 3 1 0): 16 consecutive rows read at one logical chunk land on 16
+// distinct chunk positions (row reads of 16 lanes x 16 bytes), and the 4-row x 4-chunk blocks of a
+// transpose read are spread over all 64 banks. Measured on gfx950 against the plain row-XOR key:
+// transpose reads of the forward's V pattern 63 -> 148 B/clk/CU, of the backward's 121 -> 166,
+// 16-byte row reads 105 -> 123. D = 64 (8 chunks per row) keeps the row-XOR key r & 7.
+template <int D>
+__device__ __forceinline__ int sw_key(int r) {
+  if constexpr (D >= 128) return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+  else return r & 7;
+}
+// Element offset of logical chunk c of row r.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) { return r * D + ((c ^ sw_key<D>(r)) << 3); }
+// The XOR of a read's compile-time chunk with the lane's key is left inside the loop: an opaque
+// per-iteration copy of the key stops the compiler from hoisting one address register per unrolled
+// read out of the loop (which spills at 256 registers); each read then costs one XOR-add.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

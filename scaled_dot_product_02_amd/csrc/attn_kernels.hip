@@ -179,28 +179,33 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
     us* ks = smem + stage * 2 * TILE;
     us* vs = ks + TILE;
     const int kv0 = tile * BN;
+    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
+    const us* kt = kg + (int64_t)kv0 * a.ak.row;
+    const us* vt = vg + (int64_t)kv0 * a.av.row;
+    const int klast = sq.skv - 1 - kv0;
+    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int cc = (L % CH) ^ (r & 7);
-      const int64_t kr = min(kv0 + r, sq.skv - 1);
-      dma16(kg + kr * a.ak.row + cc * 8, ks + slot * 8);
-      dma16(vg + kr * a.av.row + cc * 8, vs + slot * 8);
+      const int cc = (L % CH) ^ sw_key<D>(r);
+      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
+      dma16(kt + (rc * krs + cc * 8), ks + slot * 8);
+      dma16(vt + (rc * vrs + cc * 8), vs + slot * 8);
     }
   };
 
   const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
-  // LDS read offsets: per-lane bases for the swizzled low chunk bits, the rest is compile-time.
-  // K rows (A of S^T): row 32kb + lrow, chunk 2kk + hh  -> koff[kk & 3] + 32kb*D + 64*(kk >> 2)
-  // V^T (transpose reads): row 32kb + 16half + 4hh + rr (+8), chunk 4dt + 2(G&1) + c4/2
-  //                        -> voff[dt & 1] + (32kb + 16half)*D + 64*(dt >> 1)
-  int koff[4], voff[2];
+  // LDS addressing (see sw_key). K rows (A of S^T): row 32kb + lrow, chunk 2kk + hh -> the lane's
+  // bit hh is folded into its key, so the element offset is krow + 32kb*D + ((16kk) ^ kkey).
+  // V^T by transpose reads: k-chunk cp of key block kb covers keys 32kb + 8cp + 4hh + 0..3 and the
+  // same + 16 (both halves share a key); chunk 4dt + (2(G&1) + c4/2) with the lane part folded in.
+  const int krow = lrow * D, kkey = (sw_key<D>(lrow) ^ hh) << 3;
+  const int vrow = (4 * hh + rr) * D + 4 * (c4 & 1);
+  int vkey[2];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) koff[e] = swz_lo(lrow, 2 * e + hh, D);
-#pragma unroll
-  for (int e = 0; e < 2; ++e) voff[e] = swz_lo(4 * hh + rr, 4 * e + 2 * (G & 1) + (c4 >> 1), D) + 4 * (c4 & 1);
+  for (int cp = 0; cp < 2; ++cp) vkey[cp] = (sw_key<D>(8 * cp + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3;
   if (n_tiles > 0) issue(0, 0);
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
@@ -212,16 +217,17 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
     if (s.mask != 0 && kv0 > qw0 + 31 + delta) continue;  // tile fully masked for this wave
     const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta);
 
+    const int kx = opaque(kkey), vx0 = opaque(vkey[0]), vx1 = opaque(vkey[1]);
     v16f sacc[BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      sacc[kb] = v16f{};
+    for (int kb = 0; kb < BN / 32; ++kb) sacc[kb] = v16f{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const v8s kf = lds_read16(ks, koff[kk & 3] + 32 * kb * D + 64 * (kk >> 2));
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {  // alternate accumulators between dependent MFMAs
+        const v8s kf = lds_read16(ks, krow + 32 * kb * D + ((16 * kk) ^ kx));
         sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
       }
-    }
     // row max of the raw scores (scale c > 0); this lane's keys are kv0 + 32kb + 8(jr/4) + 4hh + jr%4
     float mt = -__builtin_inff();
 #pragma unroll
@@ -256,18 +262,20 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
         sacc[kb][jr] = p;
         l_run += p;
       }
-    // O^T += V^T P^T, 16 keys per MFMA
+    // O^T += V^T P^T, 16 keys per MFMA: k-chunk cp of block kb takes S^T registers 4cp..4cp+3 and
+    // 8+4cp..8+4cp+3, i.e. keys 32kb + 8cp + 4hh + 0..3 and the same + 16
 #pragma unroll
     for (int cb = 0; cb < BN / 16; ++cb) {
-      const int kb = cb >> 1, half = cb & 1;
-      const auto pb = pack8<T>(sacc[kb][8 * half + 0], sacc[kb][8 * half + 1], sacc[kb][8 * half + 2],
-                               sacc[kb][8 * half + 3], sacc[kb][8 * half + 4], sacc[kb][8 * half + 5],
-                               sacc[kb][8 * half + 6], sacc[kb][8 * half + 7]);
+      const int kb = cb >> 1, cp = cb & 1;
+      const auto pb = pack8<T>(sacc[kb][4 * cp + 0], sacc[kb][4 * cp + 1], sacc[kb][4 * cp + 2],
+                               sacc[kb][4 * cp + 3], sacc[kb][8 + 4 * cp + 0], sacc[kb][8 + 4 * cp + 1],
+                               sacc[kb][8 + 4 * cp + 2], sacc[kb][8 + 4 * cp + 3]);
+      const int vx = cp ? vx1 : vx0;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int o1 = voff[dt & 1] + (32 * kb + 16 * half) * D + 64 * (dt >> 1);
+        const int o1 = vrow + (32 * kb + 8 * cp) * D + ((32 * dt) ^ vx);
         const v4s lo = lds_read_tr(vs, o1);
-        const v4s hi = lds_read_tr(vs, o1 + 8 * D);
+        const v4s hi = lds_read_tr(vs, o1 + 16 * D);
         oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
       }
     }
@@ -359,28 +367,33 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
     us* ks = smem + stage * 2 * TILE;
     us* vs = ks + TILE;
     const int kv0 = tile * BN;
+    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
+    const us* kt = kg + (int64_t)kv0 * a.ak.row;
+    const us* vt = vg + (int64_t)kv0 * a.av.row;
+    const int klast = sq.skv - 1 - kv0;
+    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int cc = (L % CH) ^ (r & 7);
-      const int64_t kr = min(kv0 + r, sq.skv - 1);
-      dma16(kg + kr * a.ak.row + cc * 8, ks + slot * 8);
-      dma16(vg + kr * a.av.row + cc * 8, vs + slot * 8);
+      const int cc = (L % CH) ^ sw_key<D>(r);
+      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
+      dma16(kt + (rc * krs + cc * 8), ks + slot * 8);
+      dma16(vt + (rc * vrs + cc * 8), vs + slot * 8);
     }
   };
 
   float* mine = xch + w * 1024;
   const float* other = xch + (w ^ 4) * 1024;
   const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
-  // same offset scheme as the D <= 128 forward, shifted by this wave's half of D
-  int koff[4], voff[2];
+  // same addressing as the D <= 128 forward, shifted by this wave's half of D (whole 16-chunk groups,
+  // untouched by the swizzle)
+  const int krow = lrow * D + hf * DH, kkey = (sw_key<D>(lrow) ^ hh) << 3;
+  const int vrow = (4 * hh + rr) * D + 4 * (c4 & 1) + hf * DH;
+  int vkey[2];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) koff[e] = swz_lo(lrow, 2 * e + hh, D) + hf * DH;
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    voff[e] = swz_lo(4 * hh + rr, 4 * e + 2 * (G & 1) + (c4 >> 1), D) + 4 * (c4 & 1) + hf * DH;
+  for (int cp = 0; cp < 2; ++cp) vkey[cp] = (sw_key<D>(8 * cp + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3;
   if (n_tiles > 0) issue(0, 0);
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
@@ -390,11 +403,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
     const us* vs = ks + TILE;
     const int kv0 = j * BN;
     const bool active = s.mask == 0 || kv0 <= qw0 + 31 + delta;  // same for both waves of a pair
+    const int kx = opaque(kkey), vx0 = opaque(vkey[0]), vx1 = opaque(vkey[1]);
     v16f sacc = v16f{};
     if (active) {
 #pragma unroll
       for (int kk = 0; kk < DH / 16; ++kk) {
-        const v8s kf = lds_read16(ks, koff[kk & 3] + 64 * (kk >> 2));
+        const v8s kf = lds_read16(ks, krow + ((16 * kk) ^ kx));
         sacc = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc);
       }
 #pragma unroll
@@ -439,21 +453,16 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
       l_run += p;
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const auto pb = pack8<T>(sacc[8 * half + 0], sacc[8 * half + 1], sacc[8 * half + 2], sacc[8 * half + 3],
-                               sacc[8 * half + 4], sacc[8 * half + 5], sacc[8 * half + 6], sacc[8 * half + 7]);
+    for (int cp = 0; cp < 2; ++cp) {
+      const auto pb = pack8<T>(sacc[4 * cp + 0], sacc[4 * cp + 1], sacc[4 * cp + 2], sacc[4 * cp + 3],
+                               sacc[8 + 4 * cp + 0], sacc[8 + 4 * cp + 1], sacc[8 + 4 * cp + 2], sacc[8 + 4 * cp + 3]);
+      const int vx = cp ? vx1 : vx0;
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
-        const int o1 = voff[dt & 1] + 16 * half * D + 64 * (dt >> 1);
+        const int o1 = vrow + 8 * cp * D + ((32 * dt) ^ vx);
         const v4s lo = lds_read_tr(vs, o1);
-        const v4s hi = lds_read_tr(vs, o1 + 8 * D);
+        const v4s hi = lds_read_tr(vs, o1 + 16 * D);
         oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
-      }
-      // bound the transpose reads in flight (register pressure): 2 reads per MFMA, in order
-#pragma unroll
-      for (int dt = 0; dt < DH / 32; ++dt) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
   }
@@ -595,33 +604,36 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     float* rss = l2s + 64;
     const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
     const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
+    const us* qtile = qgh + (int64_t)qs0 * a.aq.row;
+    const us* dtile = dgh + (int64_t)qs0 * a.ao.row;
+    const int qlast = sq.sq - 1 - qs0;
+    const unsigned qrs = (unsigned)a.aq.row, ors = (unsigned)a.ao.row;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int c = (L % CH) ^ (r & 7);
-      const int64_t qr = min(qs0 + r, sq.sq - 1);
-      dma16(qgh + qr * a.aq.row + c * 8, qs + slot * 8);
-      dma16(dgh + qr * a.ao.row + c * 8, dos + slot * 8);
+      const int c = (L % CH) ^ sw_key<D>(r);
+      const unsigned rc = (unsigned)min(r, qlast);  // rows past the sequence end repeat its last row
+      dma16(qtile + (rc * qrs + c * 8), qs + slot * 8);
+      dma16(dtile + (rc * ors + c * 8), dos + slot * 8);
     }
     const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
     if (w == 0) dma4(a.lse2 + row, l2s);
     if (w == 1) dma4(a.rowsum + row, rss);
   };
 
-  // LDS read offsets (see swz_lo): Q/dO rows 16qb + l16, chunk 4kk + G -> roff[kk & 1] + 16qb*D + 64*(kk >> 1);
-  // transpose reads: rows 4G + rr (+16), chunk 2dt + c4/2 -> toff[dt & 3] + 64*(dt >> 2)
-  int roff[2], toff[4];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1);
+  // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
+  // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
+  const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
+  const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   if (n_it > 0) issue(0, 0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_it) issue(it + 1, (it + 1) & 1);
+    const int rx = opaque(rkey), tx = opaque(tkey);
     const us* qs = smem + (it & 1) * STAGE;
     const us* dos = qs + QTILE;
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
@@ -641,7 +653,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const int o = roff[kk & 1] + 16 * qb * D + 64 * (kk >> 1);
+        const int o = rrow + 16 * qb * D + ((32 * kk) ^ rx);
         const v8s qa = lds_read16(qs, o);
         const v8s da = lds_read16(dos, o);
 #pragma unroll
@@ -680,7 +692,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const int o1 = trow + ((16 * dt) ^ tx);
       const int o2 = o1 + 16 * D;
       const v8s dob = cat44(lds_read_tr(dos, o1), lds_read_tr(dos, o2));
       const v8s qbt = cat44(lds_read_tr(qs, o1), lds_read_tr(qs, o2));
@@ -771,29 +783,33 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
     const int kv0 = tile * BK;
+    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
+    const us* kt = kg + (int64_t)kv0 * a.ak.row;
+    const us* vt = vg + (int64_t)kv0 * a.av.row;
+    const int klast = sq.skv - 1 - kv0;
+    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int c = (L % CH) ^ (r & 7);
-      const int64_t kr = min(kv0 + r, sq.skv - 1);
-      dma16(kg + kr * a.ak.row + c * 8, ks + slot * 8);
-      dma16(vg + kr * a.av.row + c * 8, vs + slot * 8);
+      const int c = (L % CH) ^ sw_key<D>(r);
+      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
+      dma16(kt + (rc * krs + c * 8), ks + slot * 8);
+      dma16(vt + (rc * vrs + c * 8), vs + slot * 8);
     }
   };
 
-  // LDS read offsets as in the dK/dV pass: K/V rows 16kb + l16 -> roff; K transpose reads -> toff
-  int roff[2], toff[4];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1);
+  // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
+  // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
+  const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
+  const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   if (n_tiles > 0) issue(0, 0);
   for (int j = 0; j < n_tiles; ++j) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    const int rx = opaque(rkey), tx = opaque(tkey);
     const us* ks = smem + (j & 1) * 2 * KTILE;
     const us* vs = ks + KTILE;
     const int kv0 = j * BK;
@@ -810,7 +826,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const int o = roff[kk & 1] + 16 * kb * D + 64 * (kk >> 1);
+        const int o = rrow + 16 * kb * D + ((32 * kk) ^ rx);
         const v8s ka = lds_read16(ks, o);
         const v8s va = lds_read16(vs, o);
 #pragma unroll
@@ -841,7 +857,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const int o1 = trow + ((16 * dt) ^ tx);
       const v8s kbt = cat44(lds_read_tr(ks, o1), lds_read_tr(ks, o1 + 16 * D));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) dq[qb][dt] = Elem<T>::mma16(dsa[qb], Elem<T>::cast(kbt), dq[qb][dt]);
@@ -931,26 +947,30 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     float* rss = l2s + 64;
     const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
     const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
+    const us* qtile = qgh + (int64_t)qs0 * a.aq.row;
+    const us* dtile = dgh + (int64_t)qs0 * a.ao.row;
+    const int qlast = sq.sq - 1 - qs0;
+    const unsigned qrs = (unsigned)a.aq.row, ors = (unsigned)a.ao.row;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int c = (L % CH) ^ (r & 7);
-      const int64_t qr = min(qs0 + r, sq.sq - 1);
-      dma16(qgh + qr * a.aq.row + c * 8, qs + slot * 8);
-      dma16(dgh + qr * a.ao.row + c * 8, dos + slot * 8);
+      const int c = (L % CH) ^ sw_key<D>(r);
+      const unsigned rc = (unsigned)min(r, qlast);  // rows past the sequence end repeat its last row
+      dma16(qtile + (rc * qrs + c * 8), qs + slot * 8);
+      dma16(dtile + (rc * ors + c * 8), dos + slot * 8);
     }
     const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
     if (w == 0) dma4(a.lse2 + row, l2s);
     if (w == 1) dma4(a.rowsum + row, rss);
   };
 
-  int roff[2], toff[4];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1);
+  // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
+  // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
+  const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
+  const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   float* pbuf = xch + pr * 2 * 64 * 4;
 
   if (n_it > 0) issue(0, 0);
@@ -958,6 +978,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_it) issue(it + 1, (it + 1) & 1);
+    const int rx = opaque(rkey), tx = opaque(tkey);
     const us* qs = smem + (it & 1) * STAGE;
     const us* dos = qs + QTILE;
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
@@ -973,7 +994,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
         sv[qb] = v4f{};
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
-          sv[qb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, roff[kk & 1] + 16 * qb * D + 64 * (kk >> 1))),
+          sv[qb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, rrow + 16 * qb * D + ((32 * kk) ^ rx))),
                                   Elem<T>::cast(kvf[kk]), sv[qb]);
       }
       if (role == 0) {
@@ -1010,7 +1031,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     const us* bsrc = role == 0 ? dos : qs;  // dV += P^T dO ; dK += dS^T Q
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const int o1 = trow + ((16 * dt) ^ tx);
       const v8s bt = cat44(lds_read_tr(bsrc, o1), lds_read_tr(bsrc, o1 + 16 * D));
       acc[dt] = Elem<T>::mma16(pa, Elem<T>::cast(bt), acc[dt]);
     }
@@ -1082,23 +1103,25 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
     const int kv0 = tile * BK;
+    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
+    const us* kt = kg + (int64_t)kv0 * a.ak.row;
+    const us* vt = vg + (int64_t)kv0 * a.av.row;
+    const int klast = sq.skv - 1 - kv0;
+    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int slot = (w * NDMA + i) * 64;
       const int L = slot + lane;
       const int r = L / CH;
-      const int c = (L % CH) ^ (r & 7);
-      const int64_t kr = min(kv0 + r, sq.skv - 1);
-      dma16(kg + kr * a.ak.row + c * 8, ks + slot * 8);
-      dma16(vg + kr * a.av.row + c * 8, vs + slot * 8);
+      const int c = (L % CH) ^ sw_key<D>(r);
+      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
+      dma16(kt + (rc * krs + c * 8), ks + slot * 8);
+      dma16(vt + (rc * vrs + c * 8), vs + slot * 8);
     }
   };
 
-  int roff[2], toff[4];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) roff[e] = swz_lo(l16, 4 * e + G, D);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) toff[e] = swz_lo(4 * G + rr, 2 * e + (cc >> 1), D) + 4 * (cc & 1) + role * DH;
+  const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
+  const int trow = (4 * G + rr) * D + 4 * (cc & 1) + role * DH, tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   float* mine = xch + w * 2 * 64 * 4;
   const float* other = xch + (w ^ 4) * 2 * 64 * 4;
 
@@ -1107,6 +1130,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    const int rx = opaque(rkey), tx = opaque(tkey);
     const us* ks = smem + (j & 1) * 2 * KTILE;
     const us* vs = ks + KTILE;
     const int kv0 = j * BK;
@@ -1120,7 +1144,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
         st[kb] = v4f{};
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
-          st[kb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, roff[kk & 1] + 16 * kb * D + 64 * (kk >> 1))),
+          st[kb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, rrow + 16 * kb * D + ((32 * kk) ^ rx))),
                                   Elem<T>::cast(qdf[kk]), st[kb]);
       }
       if (role == 0) {
@@ -1157,7 +1181,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     const auto dsa = pack8<T>(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
-      const int o1 = toff[dt & 3] + 64 * (dt >> 2);
+      const int o1 = trow + ((16 * dt) ^ tx);
       const v8s kbt = cat44(lds_read_tr(ks, o1), lds_read_tr(ks, o1 + 16 * D));
       dq[dt] = Elem<T>::mma16(dsa, Elem<T>::cast(kbt), dq[dt]);
     }

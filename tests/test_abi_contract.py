@@ -131,6 +131,17 @@ def test_stride_alignment(L, which):
     expect(L, fwd(L, p), INVALID, "negative")
 
 
+@pytest.mark.parametrize("which", ["q_stride", "k_stride", "v_stride", "o_stride"])
+def test_row_stride_limit(L, which):
+    p = dense_problem()
+    getattr(p, which)[1] = 1 << 24
+    expect(L, fwd(L, p), UNSUPPORTED, "row stride")
+    getattr(p, which)[1] = (1 << 24) - 8
+    p2 = dense_problem(b=0)  # same strides, nothing to launch: accepted
+    getattr(p2, which)[1] = (1 << 24) - 8
+    assert fwd(L, p2) == OK
+
+
 @pytest.mark.parametrize("arg", ["q", "k", "v", "o"])
 def test_pointer_alignment_and_null(L, arg):
     p = dense_problem()

@@ -229,20 +229,24 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
         sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
       }
     // row max of the raw scores (scale c > 0); this lane's keys are kv0 + 32kb + 8(jr/4) + 4hh + jr%4
+    // (one branch per tile: a mask test inside the unrolled loop becomes one branch per element)
     float mt = -__builtin_inff();
+    if (need_mask) {
+      const int lim = min(sq.skv - 1, s.mask == 0 ? sq.skv : qi + delta) - kv0 - 4 * hh;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int jr = 0; jr < 16; ++jr) {
-        float x = sacc[kb][jr];
-        if (need_mask) {
-          const int key = kv0 + 32 * kb + 8 * (jr >> 2) + 4 * hh + (jr & 3);
-          const bool ok = key < sq.skv && (s.mask == 0 || key <= qi + delta);
-          x = ok ? x : -__builtin_inff();
+        for (int jr = 0; jr < 16; ++jr) {
+          const float x = 32 * kb + 8 * (jr >> 2) + (jr & 3) <= lim ? sacc[kb][jr] : -__builtin_inff();
           sacc[kb][jr] = x;
+          mt = fmaxf(mt, x);
         }
-        mt = fmaxf(mt, x);
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int jr = 0; jr < 16; ++jr) mt = fmaxf(mt, sacc[kb][jr]);
+    }
     const float m_new = pair32_max(mt) * c;
     if (wave_any(m_new > m_ref + kRescaleThreshold)) {
       const float ref = fmaxf(m_ref, m_new);
@@ -663,6 +667,19 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
+    if (need_mask) {  // one branch per tile (a test inside the unrolled loop branches per element)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q = qs0 + 16 * qb + 4 * G + i;
+            const int key = kw0 + 16 * kb + l16;
+            const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
+            sv[qb][kb][i] = ok ? sv[qb][kb][i] : -__builtin_inff();  // exp2 -> exactly 0
+          }
+    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const v4f l2 = *reinterpret_cast<const v4f*>(l2s + 16 * qb + 4 * G);
@@ -671,13 +688,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p = fast_exp2(sv[qb][kb][i] * s.scale_log2 - l2[i]);
-          if (need_mask) {
-            const int q = qs0 + 16 * qb + 4 * G + i;
-            const int key = kw0 + 16 * kb + l16;
-            const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
-            p = ok ? p : 0.f;
-          }
+          const float p = fast_exp2(sv[qb][kb][i] * s.scale_log2 - l2[i]);
           sv[qb][kb][i] = p;
           dp[qb][kb][i] = p * (dp[qb][kb][i] - dr[i]);
         }
@@ -836,6 +847,25 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[kb][qb][i] = fast_exp2(st[kb][qb][i] * s.scale_log2 - l2[qb]);
+    if (need_mask) {  // one branch per tile (a test inside the unrolled loop branches per element)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q = qw0 + 16 * qb + l16;
+            const int key = kv0 + 16 * kb + 4 * G + i;
+            const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta);
+            st[kb][qb][i] = ok ? st[kb][qb][i] : 0.f;
+          }
+    }
     typename Elem<T>::op8 dsa[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -843,16 +873,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = fast_exp2(st[kb][qb][i] * s.scale_log2 - l2[qb]);
-          if (need_mask) {
-            const int q = qw0 + 16 * qb + l16;
-            const int key = kv0 + 16 * kb + 4 * G + i;
-            const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta);
-            p = ok ? p : 0.f;
-          }
-          ds[kb][i] = p * (dpt[kb][qb][i] - dr[qb]);
-        }
+        for (int i = 0; i < 4; ++i) ds[kb][i] = st[kb][qb][i] * (dpt[kb][qb][i] - dr[qb]);
       dsa[qb] = pack8<T>(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
     }
 #pragma unroll

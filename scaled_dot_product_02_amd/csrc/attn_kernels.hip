@@ -56,6 +56,55 @@ __device__ __forceinline__ Seq seq_info(const AttnShape& s, int b) {
   return r;
 }
 
+// HBM -> LDS copy of one tile of two tensors X and Y (ROWS rows of D 16-bit elements each, rows
+// stored with swizzled 16-byte chunks) by one wave: its NDMA 64-lane slots, slot wslot*NDMA + i
+// covering 64 consecutive chunks. Each copy is a uniform 64-bit tile base plus a 32-bit per-lane
+// byte offset (row strides < 2^24 elements, checked by the host), the scalar-base form of the load.
+// KEEP: the per-lane offsets of full tiles stay in registers (2*NDMA of them); otherwise each tile
+// clamps the lane's row and forms its offsets (a few VALU operations per copy) where registers are
+// short. A tile that runs past the sequence end clamps each row to its last valid row (the repeated
+// rows are masked by the kernels).
+template <int D, int ROWS, int NDMA, bool KEEP = true>
+struct TileDma {
+  static constexpr int CH = D / 8;
+  static_assert((ROWS * CH) % (NDMA * 64) == 0, "a tile is a whole number of wave slots");
+  unsigned xo[KEEP ? NDMA : 1], yo[KEEP ? NDMA : 1];
+  int slot0, lane;
+  unsigned xrs, yrs;
+  __device__ __forceinline__ TileDma(int wslot, int lane_, int64_t xrow, int64_t yrow)
+      : slot0(wslot * NDMA * 64), lane(lane_), xrs((unsigned)xrow), yrs((unsigned)yrow) {
+    if constexpr (KEEP) {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) offsets(lane, i, ROWS, xo[i], yo[i]);
+    }
+  }
+  // byte offsets of slot i's chunk for this lane, its row clamped to last
+  __device__ __forceinline__ void offsets(int ln, int i, int last, unsigned& xb, unsigned& yb) const {
+    const int L = slot0 + i * 64 + ln;
+    const int r = L / CH;
+    const unsigned c = (unsigned)((L % CH) ^ sw_key<D>(r));
+    const unsigned rc = (unsigned)min(r, last);
+    xb = (rc * xrs + c * 8) * 2;
+    yb = (rc * yrs + c * 8) * 2;
+  }
+  // xt, yt: the tile's first rows; last: index of the tile's last valid row (>= 0)
+  __device__ __forceinline__ void copy(const us* xt, const us* yt, int last, us* xs, us* ys) const {
+    const bool full = last >= ROWS - 1;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      unsigned xb, yb;
+      if (KEEP && full) {  // opaque: keeps the 32-bit offset (not a hoisted 64-bit copy) in the load
+        xb = (unsigned)opaque((int)xo[KEEP ? i : 0]);
+        yb = (unsigned)opaque((int)yo[KEEP ? i : 0]);
+      } else {
+        offsets(lane, i, last, xb, yb);
+      }
+      dma16((const char*)xt + xb, xs + (slot0 + i * 64) * 8);
+      dma16((const char*)yt + yb, ys + (slot0 + i * 64) * 8);
+    }
+  }
+};
+
 template <typename T> __device__ __forceinline__ us nan_bits();
 template <> __device__ __forceinline__ us nan_bits<__bf16>() { return 0x7FC0; }
 template <> __device__ __forceinline__ us nan_bits<_Float16>() { return 0x7E00; }
@@ -175,25 +224,12 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   float m_ref = -__builtin_inff();  // scaled (log2-domain) reference of this row
   float l_run = 0.f;                // this lane's half of the row sum, relative to m_ref
 
+  const TileDma<D, BN, NDMA> dma(w, lane, a.ak.row, a.av.row);
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * TILE;
     us* vs = ks + TILE;
     const int kv0 = tile * BN;
-    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
-    const us* kt = kg + (int64_t)kv0 * a.ak.row;
-    const us* vt = vg + (int64_t)kv0 * a.av.row;
-    const int klast = sq.skv - 1 - kv0;
-    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot = (w * NDMA + i) * 64;
-      const int L = slot + lane;
-      const int r = L / CH;
-      const int cc = (L % CH) ^ sw_key<D>(r);
-      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
-      dma16(kt + (rc * krs + cc * 8), ks + slot * 8);
-      dma16(vt + (rc * vrs + cc * 8), vs + slot * 8);
-    }
+    dma.copy(kg + (int64_t)kv0 * a.ak.row, vg + (int64_t)kv0 * a.av.row, sq.skv - 1 - kv0, ks, vs);
   };
 
   const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
@@ -228,6 +264,14 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
         const v8s kf = lds_read16(ks, krow + 32 * kb * D + ((16 * kk) ^ kx));
         sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
       }
+    // schedule: the K-fragment reads run two ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // mask 0x100: LDS reads
+#pragma unroll
+    for (int i = 0; i < D / 16 * BN / 32 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // mask 0x008: MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     // row max of the raw scores (scale c > 0); this lane's keys are kv0 + 32kb + 8(jr/4) + 4hh + jr%4
     // (one branch per tile: a mask test inside the unrolled loop becomes one branch per element)
     float mt = -__builtin_inff();
@@ -367,25 +411,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   float m_ref = -__builtin_inff();
   float l_run = 0.f;
 
+  const TileDma<D, BN, NDMA, (D < 512)> dma(w, lane, a.ak.row, a.av.row);  // registers are short at D = 512
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * TILE;
     us* vs = ks + TILE;
     const int kv0 = tile * BN;
-    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
-    const us* kt = kg + (int64_t)kv0 * a.ak.row;
-    const us* vt = vg + (int64_t)kv0 * a.av.row;
-    const int klast = sq.skv - 1 - kv0;
-    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot = (w * NDMA + i) * 64;
-      const int L = slot + lane;
-      const int r = L / CH;
-      const int cc = (L % CH) ^ sw_key<D>(r);
-      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
-      dma16(kt + (rc * krs + cc * 8), ks + slot * 8);
-      dma16(vt + (rc * vrs + cc * 8), vs + slot * 8);
-    }
+    dma.copy(kg + (int64_t)kv0 * a.ak.row, vg + (int64_t)kv0 * a.av.row, sq.skv - 1 - kv0, ks, vs);
   };
 
   float* mine = xch + w * 1024;
@@ -598,6 +629,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       dv[kb][dt] = v4f{};
     }
 
+  const TileDma<D, BQ, NDMA, (D != 128)> dma(w, lane, a.aq.row, a.ao.row);  // registers are short at D = 128
   auto issue = [&](int it, int stage) {
     const int hi = it / nq, qt = qt0 + it % nq;
     const int h = g * s.group + hi;
@@ -608,21 +640,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     float* rss = l2s + 64;
     const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
     const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
-    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
-    const us* qtile = qgh + (int64_t)qs0 * a.aq.row;
-    const us* dtile = dgh + (int64_t)qs0 * a.ao.row;
-    const int qlast = sq.sq - 1 - qs0;
-    const unsigned qrs = (unsigned)a.aq.row, ors = (unsigned)a.ao.row;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot = (w * NDMA + i) * 64;
-      const int L = slot + lane;
-      const int r = L / CH;
-      const int c = (L % CH) ^ sw_key<D>(r);
-      const unsigned rc = (unsigned)min(r, qlast);  // rows past the sequence end repeat its last row
-      dma16(qtile + (rc * qrs + c * 8), qs + slot * 8);
-      dma16(dtile + (rc * ors + c * 8), dos + slot * 8);
-    }
+    dma.copy(qgh + (int64_t)qs0 * a.aq.row, dgh + (int64_t)qs0 * a.ao.row, sq.sq - 1 - qs0, qs, dos);
     const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
     if (w == 0) dma4(a.lse2 + row, l2s);
     if (w == 1) dma4(a.rowsum + row, rss);
@@ -790,25 +808,12 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) dq[qb][dt] = v4f{};
 
+  const TileDma<D, BK, NDMA> dma(w, lane, a.ak.row, a.av.row);
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
     const int kv0 = tile * BK;
-    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
-    const us* kt = kg + (int64_t)kv0 * a.ak.row;
-    const us* vt = vg + (int64_t)kv0 * a.av.row;
-    const int klast = sq.skv - 1 - kv0;
-    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot = (w * NDMA + i) * 64;
-      const int L = slot + lane;
-      const int r = L / CH;
-      const int c = (L % CH) ^ sw_key<D>(r);
-      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
-      dma16(kt + (rc * krs + c * 8), ks + slot * 8);
-      dma16(vt + (rc * vrs + c * 8), vs + slot * 8);
-    }
+    dma.copy(kg + (int64_t)kv0 * a.ak.row, vg + (int64_t)kv0 * a.av.row, sq.skv - 1 - kv0, ks, vs);
   };
 
   // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
@@ -958,6 +963,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = v4f{};
 
+  const TileDma<D, BQ, NDMA> dma(w, lane, a.aq.row, a.ao.row);
   auto issue = [&](int it, int stage) {
     const int hi = it / nq, qt = qt0 + it % nq;
     const int h = g * s.group + hi;
@@ -968,21 +974,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     float* rss = l2s + 64;
     const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
     const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
-    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
-    const us* qtile = qgh + (int64_t)qs0 * a.aq.row;
-    const us* dtile = dgh + (int64_t)qs0 * a.ao.row;
-    const int qlast = sq.sq - 1 - qs0;
-    const unsigned qrs = (unsigned)a.aq.row, ors = (unsigned)a.ao.row;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot = (w * NDMA + i) * 64;
-      const int L = slot + lane;
-      const int r = L / CH;
-      const int c = (L % CH) ^ sw_key<D>(r);
-      const unsigned rc = (unsigned)min(r, qlast);  // rows past the sequence end repeat its last row
-      dma16(qtile + (rc * qrs + c * 8), qs + slot * 8);
-      dma16(dtile + (rc * ors + c * 8), dos + slot * 8);
-    }
+    dma.copy(qgh + (int64_t)qs0 * a.aq.row, dgh + (int64_t)qs0 * a.ao.row, sq.sq - 1 - qs0, qs, dos);
     const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
     if (w == 0) dma4(a.lse2 + row, l2s);
     if (w == 1) dma4(a.rowsum + row, rss);
@@ -1120,25 +1112,12 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) dq[dt] = v4f{};
 
+  const TileDma<D, BK, NDMA> dma(w, lane, a.ak.row, a.av.row);
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
     const int kv0 = tile * BK;
-    // tile base (uniform, 64-bit) + per-lane 32-bit offsets; row strides < 2^24 (checked by the host)
-    const us* kt = kg + (int64_t)kv0 * a.ak.row;
-    const us* vt = vg + (int64_t)kv0 * a.av.row;
-    const int klast = sq.skv - 1 - kv0;
-    const unsigned krs = (unsigned)a.ak.row, vrs = (unsigned)a.av.row;
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int slot = (w * NDMA + i) * 64;
-      const int L = slot + lane;
-      const int r = L / CH;
-      const int c = (L % CH) ^ sw_key<D>(r);
-      const unsigned rc = (unsigned)min(r, klast);  // rows past the sequence end repeat its last row
-      dma16(kt + (rc * krs + c * 8), ks + slot * 8);
-      dma16(vt + (rc * vrs + c * 8), vs + slot * 8);
-    }
+    dma.copy(kg + (int64_t)kv0 * a.ak.row, vg + (int64_t)kv0 * a.av.row, sq.skv - 1 - kv0, ks, vs);
   };
 
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;

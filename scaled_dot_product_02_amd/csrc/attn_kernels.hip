@@ -56,6 +56,41 @@ __device__ __forceinline__ Seq seq_info(const AttnShape& s, int b) {
   return r;
 }
 
+// Query-side walk of the dK/dV passes: query tiles qt0 .. qt0+nq-1 of each q-head of a GQA group in
+// turn, one step per loaded tile. Running pointers to the tile's Q and dO rows and to the head's
+// lse2 / D rows replace a division and several 64-bit products per tile.
+template <int BQ>
+struct QueryWalk {
+  const us *qh, *oh, *qp, *op;
+  const float *l2, *rs;
+  int64_t qstep, ostep, qhead, ohead, nrows;
+  int qt, qt0, qt_end;
+  __device__ __forceinline__ QueryWalk(const BwdArgs& a, bool packed, int b, const Seq& sq, int h0, int qt0_, int nq)
+      : qstep((int64_t)BQ * a.aq.row), ostep((int64_t)BQ * a.ao.row), qhead(a.aq.head), ohead(a.ao.head),
+        nrows(a.nrows), qt(qt0_), qt0(qt0_), qt_end(qt0_ + nq) {
+    qh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h0 * a.aq.head;
+    oh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h0 * a.ao.head;
+    qp = qh + qt0 * qstep;
+    op = oh + qt0 * ostep;
+    const int64_t row0 = (int64_t)h0 * a.nrows + (packed ? sq.tq0 : (int64_t)b * a.s.sq);
+    l2 = a.lse2 + row0;
+    rs = a.rowsum + row0;
+  }
+  __device__ __forceinline__ void next() {
+    qp += qstep;
+    op += ostep;
+    if (++qt == qt_end) {  // next q-head of the group
+      qt = qt0;
+      qh += qhead;
+      oh += ohead;
+      qp = qh + qt0 * qstep;
+      op = oh + qt0 * ostep;
+      l2 += nrows;
+      rs += nrows;
+    }
+  }
+};
+
 // HBM -> LDS copy of one tile of two tensors X and Y (ROWS rows of D 16-bit elements each, rows
 // stored with swizzled 16-byte chunks) by one wave: its NDMA 64-lane slots, slot wslot*NDMA + i
 // covering 64 consecutive chunks. Each copy is a uniform 64-bit tile base plus a 32-bit per-lane
@@ -606,7 +641,6 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int qt0 = q_lo / BQ;
   const int nq = max(0, (sq.sq + BQ - 1) / BQ - qt0);
   const int n_it = nq * s.group;
-  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
 
   const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
   const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
@@ -630,37 +664,38 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 
   const TileDma<D, BQ, NDMA, (D != 128)> dma(w, lane, a.aq.row, a.ao.row);  // registers are short at D = 128
-  auto issue = [&](int it, int stage) {
-    const int hi = it / nq, qt = qt0 + it % nq;
-    const int h = g * s.group + hi;
-    const int qs0 = qt * BQ;
+  QueryWalk<BQ> ld(a, packed, b, sq, g * s.group, qt0, nq);
+  const int qt_end = qt0 + nq;
+  auto issue = [&](int stage) {
+    const int qs0 = ld.qt * BQ;
     us* qs = smem + stage * STAGE;
     us* dos = qs + QTILE;
     float* l2s = reinterpret_cast<float*>(dos + QTILE);
     float* rss = l2s + 64;
-    const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
-    const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
-    dma.copy(qgh + (int64_t)qs0 * a.aq.row, dgh + (int64_t)qs0 * a.ao.row, sq.sq - 1 - qs0, qs, dos);
-    const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
-    if (w == 0) dma4(a.lse2 + row, l2s);
-    if (w == 1) dma4(a.rowsum + row, rss);
+    dma.copy(ld.qp, ld.op, sq.sq - 1 - qs0, qs, dos);
+    const int r = min(qs0 + lane, sq.sq - 1);
+    if (w == 0) dma4(ld.l2 + r, l2s);
+    if (w == 1) dma4(ld.rs + r, rss);
+    ld.next();
   };
 
   // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
   // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
-  if (n_it > 0) issue(0, 0);
+  int qt_c = qt0;  // query tile of the iteration
+  if (n_it > 0) issue(0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
     __syncthreads();
-    if (it + 1 < n_it) issue(it + 1, (it + 1) & 1);
+    if (it + 1 < n_it) issue((it + 1) & 1);
     const int rx = opaque(rkey), tx = opaque(tkey);
     const us* qs = smem + (it & 1) * STAGE;
     const us* dos = qs + QTILE;
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
     const float* rss = l2s + 64;
-    const int qs0 = (qt0 + it % nq) * BQ;
+    const int qs0 = qt_c * BQ;
+    qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
     if (kw0 >= sq.skv) continue;
     if (s.mask != 0 && qs0 + BQ - 1 + delta < kw0) continue;  // no row of the tile sees these keys
     const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1);
@@ -947,7 +982,6 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int qt0 = q_lo / BQ;
   const int nq = max(0, (sq.sq + BQ - 1) / BQ - qt0);
   const int n_it = nq * s.group;
-  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
 
   // role 0 keeps K, role 1 keeps V (B operands: key kw0 + l16, d = 32kk + 8G + t)
   const us* kvg = role == 0 ? (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head
@@ -964,20 +998,19 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = v4f{};
 
   const TileDma<D, BQ, NDMA> dma(w, lane, a.aq.row, a.ao.row);
-  auto issue = [&](int it, int stage) {
-    const int hi = it / nq, qt = qt0 + it % nq;
-    const int h = g * s.group + hi;
-    const int qs0 = qt * BQ;
+  QueryWalk<BQ> ld(a, packed, b, sq, g * s.group, qt0, nq);
+  const int qt_end = qt0 + nq;
+  auto issue = [&](int stage) {
+    const int qs0 = ld.qt * BQ;
     us* qs = smem + stage * STAGE;
     us* dos = qs + QTILE;
     float* l2s = reinterpret_cast<float*>(dos + QTILE);
     float* rss = l2s + 64;
-    const us* qgh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
-    const us* dgh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
-    dma.copy(qgh + (int64_t)qs0 * a.aq.row, dgh + (int64_t)qs0 * a.ao.row, sq.sq - 1 - qs0, qs, dos);
-    const int64_t row = (int64_t)h * a.nrows + rowbase + min(qs0 + lane, sq.sq - 1);
-    if (w == 0) dma4(a.lse2 + row, l2s);
-    if (w == 1) dma4(a.rowsum + row, rss);
+    dma.copy(ld.qp, ld.op, sq.sq - 1 - qs0, qs, dos);
+    const int r = min(qs0 + lane, sq.sq - 1);
+    if (w == 0) dma4(ld.l2 + r, l2s);
+    if (w == 1) dma4(ld.rs + r, rss);
+    ld.next();
   };
 
   // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
@@ -986,17 +1019,19 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   float* pbuf = xch + pr * 2 * 64 * 4;
 
-  if (n_it > 0) issue(0, 0);
+  int qt_c = qt0;  // query tile of the iteration
+  if (n_it > 0) issue(0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
     __syncthreads();
-    if (it + 1 < n_it) issue(it + 1, (it + 1) & 1);
+    if (it + 1 < n_it) issue((it + 1) & 1);
     const int rx = opaque(rkey), tx = opaque(tkey);
     const us* qs = smem + (it & 1) * STAGE;
     const us* dos = qs + QTILE;
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
     const float* rss = l2s + 64;
-    const int qs0 = (qt0 + it % nq) * BQ;
+    const int qs0 = qt_c * BQ;
+    qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
     const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0);
     const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1);
     v4f sv[2];  // role 0: S then P; role 1: dP then dS
@@ -1113,11 +1148,17 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   for (int dt = 0; dt < DH / 16; ++dt) dq[dt] = v4f{};
 
   const TileDma<D, BK, NDMA> dma(w, lane, a.ak.row, a.av.row);
+  // issue() is called for tiles 0, 1, 2, ... in order: running tile pointers
+  const int64_t kstep = (int64_t)BK * a.ak.row, vstep = (int64_t)BK * a.av.row;
+  const us* k_ld = kg;
+  const us* v_ld = vg;
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
     const int kv0 = tile * BK;
-    dma.copy(kg + (int64_t)kv0 * a.ak.row, vg + (int64_t)kv0 * a.av.row, sq.skv - 1 - kv0, ks, vs);
+    dma.copy(k_ld, v_ld, sq.skv - 1 - kv0, ks, vs);
+    k_ld += kstep;
+    v_ld += vstep;
   };
 
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;

@@ -32,10 +32,10 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
 # source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
 TRAFFIC = {
-    ("dense_d128", "bwd_dkdv"): {"src_sha1": "2bb7467cf3a3", "bytes": 855367009},
-    ("dense_d128", "fwd"): {"src_sha1": "2bb7467cf3a3", "bytes": 681779429},
-    ("dense_d128", "bwd_dq"): {"src_sha1": "2bb7467cf3a3", "bytes": 614351881},
-    ("dense_d128", "bwd_pre"): {"src_sha1": "2bb7467cf3a3", "bytes": 159446865},
+    ("dense_d128", "bwd_dkdv"): {"src_sha1": "beccd0513e32", "bytes": 697622702},
+    ("dense_d128", "fwd"): {"src_sha1": "beccd0513e32", "bytes": 806544378},
+    ("dense_d128", "bwd_dq"): {"src_sha1": "beccd0513e32", "bytes": 765277135},
+    ("dense_d128", "bwd_pre"): {"src_sha1": "beccd0513e32", "bytes": 159437553},
 }
 
 

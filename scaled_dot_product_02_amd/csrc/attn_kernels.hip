@@ -282,13 +282,15 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
-    const us* ks = smem + (j & 1) * 2 * TILE;
-    const us* vs = ks + TILE;
+    const int sb = (j & 1) * 4 * TILE;  // stage, bytes; K tile at sb, V tile at sb + 2*TILE
     const int kv0 = j * BN;
     if (s.mask != 0 && kv0 > qw0 + 31 + delta) continue;  // tile fully masked for this wave
     const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta);
 
-    const int kx = opaque(kkey), vx0 = opaque(vkey[0]), vx1 = opaque(vkey[1]);
+    // per-tile byte bases: the stage and row parts never touch the swizzled chunk bits, so each read
+    // below is one XOR with a constant (plus an immediate offset)
+    const int kb_ = opaque(2 * (krow + kkey)) + sb;
+    const int vb0 = opaque(2 * (vrow + vkey[0])) + sb + 2 * TILE, vb1 = opaque(2 * (vrow + 8 * D + vkey[1])) + sb + 2 * TILE;
     v16f sacc[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) sacc[kb] = v16f{};
@@ -296,7 +298,7 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {  // alternate accumulators between dependent MFMAs
-        const v8s kf = lds_read16(ks, krow + 32 * kb * D + ((16 * kk) ^ kx));
+        const v8s kf = lds_read16_at(smem, (kb_ ^ (32 * kk)) + 64 * kb * D);
         sacc[kb] = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc[kb]);
       }
     // schedule: the K-fragment reads run two ahead of the MFMAs that consume them
@@ -353,12 +355,12 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
       const auto pb = pack8<T>(sacc[kb][4 * cp + 0], sacc[kb][4 * cp + 1], sacc[kb][4 * cp + 2],
                                sacc[kb][4 * cp + 3], sacc[kb][8 + 4 * cp + 0], sacc[kb][8 + 4 * cp + 1],
                                sacc[kb][8 + 4 * cp + 2], sacc[kb][8 + 4 * cp + 3]);
-      const int vx = cp ? vx1 : vx0;
+      const int vb = cp ? vb1 : vb0;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int o1 = vrow + (32 * kb + 8 * cp) * D + ((32 * dt) ^ vx);
-        const v4s lo = lds_read_tr(vs, o1);
-        const v4s hi = lds_read_tr(vs, o1 + 16 * D);
+        const int o1 = (vb ^ (64 * dt)) + 64 * kb * D;
+        const v4s lo = lds_read_tr_at(smem, o1);
+        const v4s hi = lds_read_tr_at(smem, o1 + 32 * D);
         oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
       }
     }
@@ -679,20 +681,23 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     ld.next();
   };
 
-  // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
-  // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
+  // LDS offsets (elements; the reads take twice these in bytes). Row reads: Q/dO row 16m + l16, logical
+  // chunk 4kk + G at ((stage + rrow + rkey) ^ 32kk) + 16m*D; transpose reads: rows 4G + rr (+16), chunk
+  // 2dt + cc/2 at (stage + trow + tkey) ^ 16dt (+16D). The swizzled chunk bits (element bits
+  // 3..log2(D)-1) are the only bits the keys and the XOR constants touch; the stage, row and tile offsets
+  // are zero there, so adding them first and XOR-ing after gives the same offset: one XOR per read.
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
+  static_assert((STAGE & (D - 1)) == 0 && (QTILE & (D - 1)) == 0, "stage offsets must leave the chunk bits alone");
   int qt_c = qt0;  // query tile of the iteration
   if (n_it > 0) issue(0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_it) issue((it + 1) & 1);
-    const int rx = opaque(rkey), tx = opaque(tkey);
-    const us* qs = smem + (it & 1) * STAGE;
-    const us* dos = qs + QTILE;
-    const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
+    const int sb = (it & 1) * STAGE;
+    const int rb = opaque(2 * (rrow + rkey)) + 2 * sb, tb = opaque(2 * (trow + tkey)) + 2 * sb;  // bytes
+    const float* l2s = reinterpret_cast<const float*>(smem + sb + 2 * QTILE);
     const float* rss = l2s + 64;
     const int qs0 = qt_c * BQ;
     qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
@@ -710,9 +715,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const int o = rrow + 16 * qb * D + ((32 * kk) ^ rx);
-        const v8s qa = lds_read16(qs, o);
-        const v8s da = lds_read16(dos, o);
+        const int o = (rb ^ (64 * kk)) + 32 * qb * D;
+        const v8s qa = lds_read16_at(smem, o);
+        const v8s da = lds_read16_at(smem, o + 2 * QTILE);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           sv[qb][kb] = Elem<T>::mma16(Elem<T>::cast(qa), Elem<T>::cast(kf[kb][kk]), sv[qb][kb]);
@@ -721,14 +726,16 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     if (need_mask) {  // one branch per tile (a test inside the unrolled loop branches per element)
+      // (opaque: the index arithmetic stays inside the branch instead of being hoisted onto every tile)
+      const int ql = opaque(qs0 + 4 * G), kl = opaque(kw0 + l16);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int q = qs0 + 16 * qb + 4 * G + i;
-            const int key = kw0 + 16 * kb + l16;
+            const int q = ql + 16 * qb + i;
+            const int key = kl + 16 * kb;
             const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
             sv[qb][kb][i] = ok ? sv[qb][kb][i] : -__builtin_inff();  // exp2 -> exactly 0
           }
@@ -756,10 +763,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = trow + ((16 * dt) ^ tx);
-      const int o2 = o1 + 16 * D;
-      const v8s dob = cat44(lds_read_tr(dos, o1), lds_read_tr(dos, o2));
-      const v8s qbt = cat44(lds_read_tr(qs, o1), lds_read_tr(qs, o2));
+      const int o1 = tb ^ (32 * dt);
+      const v8s dob = cat44(lds_read_tr_at(smem, o1 + 2 * QTILE), lds_read_tr_at(smem, o1 + 2 * QTILE + 32 * D));
+      const v8s qbt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         dv[kb][dt] = Elem<T>::mma16(pa[kb], Elem<T>::cast(dob), dv[kb][dt]);

@@ -19,6 +19,8 @@ sdpa_ref   the float64 definition (forward, backward, per-row sampling)
 floor      the in-dtype computation used for the "2 x floor" criterion of
            pull request 3527, section Verification (torch CPU, fp32 math with
            every intermediate rounded to the operand dtype)
+merge      the combination of attention results over disjoint key chunks
+           (the p2p ring step of pull request 3527, section Scope)
 
 Parity status of every function is pinned by tests/test_oracle_pins.py; none
 is "parity unpinned" except the pages' own example values, which the pages do
@@ -36,3 +38,4 @@ from .sdpa_ref import (  # noqa: F401
     sdpa_bwd,
     count_allowed_pairs,
 )
+from .merge import merge, lse_like_o  # noqa: F401

@@ -90,3 +90,20 @@ def floor_units(q, k, v, do, mask, scale, dtype, units, cu_seqlens_q=None, cu_se
         out[(b, g)] = dict(o=torch.stack(os_), lse=torch.stack(ls_), dq=torch.stack(dqs),
                            dk=dk_acc.to(dtype).to(torch.float32), dv=dv_acc.to(dtype).to(torch.float32))
     return out
+
+
+def floor_merge(o_parts, lse_parts, dtype):
+    """The merge of per-chunk results (oracle.merge) with fp32 arithmetic and the output O rounded to
+    dtype; LSE stays fp32. o_parts: torch tensors of dtype [..., D]; lse_parts: fp32 [...].
+    Returns fp32 (O, LSE)."""
+    lse = torch.stack([x.to(torch.float32) for x in lse_parts])
+    o = torch.stack([x.to(torch.float32) for x in o_parts])
+    m = lse.max(dim=0).values
+    live = torch.isfinite(m)
+    m0 = torch.where(live, m, torch.zeros_like(m))
+    w = torch.exp(lse - m0)
+    tot = torch.where(live, w.sum(dim=0), torch.ones_like(m))
+    out_lse = torch.where(live, m0 + torch.log(tot), torch.full_like(m, float("-inf")))
+    frac = torch.where(live, w / tot, torch.zeros_like(w))
+    out_o = (frac[..., None] * o).sum(dim=0).to(dtype).to(torch.float32)
+    return out_o, out_lse

@@ -13,7 +13,10 @@ timed region; the kernel with the largest per-step time is reported under
 dQ pass 2D per pair, which sum to the 14D credited per step; the dQ pass's second
 S/dP recompute is not credited) against the dense bf16/fp16 MFMA peak of 2.5 PFLOP/s.
 "cpu_baseline" times the float64 CPU oracle on a bounded sample of the same
-workload. Prints one JSON line on stdout; diagnostics go to stderr.
+workload. The default run also reports, under "extra", the D=512 workload and
+attn_merge (two forward results combined, the ring step) on the dense D=128
+query side, the latter against the HBM peak. Prints one JSON line on stdout;
+diagnostics go to stderr.
 """
 
 import argparse
@@ -159,6 +162,38 @@ def run(w, steps, warmup, want_events=True):
     return dict(x=x, ms_step=ms_step, kern_ms=kern_ms, pairs=pairs, nrows=p.total_q if w.packed else w.batch * w.sq)
 
 
+def merge_measure(w, parts=2, steps=20, warmup=3):
+    """attn_merge of `parts` forward results over w's query side (the ring step's combination).
+
+    HBM-bound: per (row, head) it reads parts x (2*D + 4) bytes and writes 2*D + 4. Returns the
+    average launch time (HIP events on the launch stream) and the achieved GB/s against 8 TB/s.
+    """
+    import torch
+    import scaled_dot_product_02_amd as sd
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(7)
+    shape = (w.batch, w.sq, w.hq, w.d)
+    o_parts = [torch.randn(shape, generator=g).to(w.torch_dtype).to(dev) for _ in range(parts)]
+    lse_parts = [(torch.randn(w.batch, w.hq, w.sq, generator=g) * 4).to(dev) for _ in range(parts)]
+    out = torch.empty(shape, dtype=w.torch_dtype, device=dev)
+    lse = torch.empty(w.batch, w.hq, w.sq, dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        sd.attn_merge(o_parts, lse_parts, out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        sd.attn_merge(o_parts, lse_parts, out=out, lse=lse)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    nbytes = w.batch * w.sq * w.hq * (parts + 1) * (2 * w.d + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"what": f"attn_merge of {parts} forward results, query side of {w.name}", "parts": parts,
+            "us": round(ms * 1e3, 2), "bytes": nbytes, "GB/s": round(gbs, 1), "peak": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +202,8 @@ def main():
     ap.add_argument("--workload", default="dense_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the informational D=512 line")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only time attn_merge of two forward results (dense_d128 query side) and print its line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (calibrates HBM byte counters) and exit")
     args = ap.parse_args()
@@ -193,6 +230,9 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     w = WORKLOADS[args.workload]
+    if args.merge_only:
+        print(json.dumps({"merge": merge_measure(w, steps=args.steps, warmup=args.warmup)}), flush=True)
+        return
     log(f"workload {w.name}: {w.note}")
     r = run(w, args.steps, args.warmup)
     d, pairs = w.d, r["pairs"]
@@ -236,7 +276,8 @@ def main():
         km2 = r2["kern_ms"]
         out["extra"] = {"dense_d512": {"tflops": round(f2 / (r2["ms_step"] * 1e-3) / 1e12, 2),
                                        "ms_per_step": round(r2["ms_step"], 4),
-                                       "kernel_ms": {n: round(t, 4) for n, t in km2.items()}}}
+                                       "kernel_ms": {n: round(t, 4) for n, t in km2.items()}},
+                        "merge": merge_measure(w)}
     if not args.no_cpu_baseline:
         log("timing the float64 CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, r["x"])

@@ -143,6 +143,25 @@ attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k,
                           const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* Merge of attention results over disjoint key chunks: the combination step of the p2p (ring)
+ * context-parallel mode, which shards the keys across steps (pull request 3527, section Scope), with
+ * neutral statistics for empty blocks (pull request 3693, Description). o_parts[k], lse_parts[k]
+ * (k < n_parts, 1 <= n_parts <= ATTN_MERGE_MAX_PARTS; host arrays of device pointers) are attn_fwd
+ * results for the same queries against disjoint key sets, laid out as attn_fwd writes O (p->o_stride)
+ * and LSE. Writes, per query row and head,
+ *   LSE = log(sum_k exp(LSE_k))                (natural log, fp32)
+ *   O   = sum_k exp(LSE_k - LSE) * O_k         (fp32 arithmetic, rounded to p->dtype)
+ * into o (p->o_stride) and lse. Parts with LSE_k = -inf contribute nothing; rows where every part is
+ * -inf get O = 0, LSE = -inf. The result equals one attn_fwd over the union of the key sets (up to the
+ * rounding of the parts), and merging is associative, so any number of chunks can be merged in steps.
+ * Only the query side of p is used: abi_version, dtype, batch, heads_q, head_dim, max_seqlen_q,
+ * o_stride, and for packed batches cu_seqlens_q (marks the layout; not read) and total_q. o may be
+ * exactly one of the o_parts and lse exactly one of the lse_parts (in-place accumulation); any other
+ * overlap of an output with an input or with the other output is ATTN_E_OVERLAP. No workspace. */
+#define ATTN_MERGE_MAX_PARTS 8
+attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* const* o_parts,
+                         const float* const* lse_parts, void* o, float* lse, void* stream);
+
 const char* attn_status_str(attn_status_t s); /* static string naming the status code          */
 const char* attn_last_error(void);            /* thread-local reason for this thread's last error */
 int32_t attn_abi_version(void);               /* ATTN_ABI_VERSION of the built library           */

@@ -3,7 +3,8 @@
 The hot path (forward, backward preprocess, dK/dV pass, dQ pass) is hand-written
 HIP in csrc/, behind the C-ABI of include/attn.h, built into libsdpa02.so. This
 package exposes that ABI to Python under the same names (argument marshalling
-only) plus the seeded synthetic workloads used by the tests and bench.py.
+only) plus the seeded synthetic workloads used by the tests and bench.py. attn_merge
+combines forward results over disjoint key chunks (the ring context-parallel step).
 """
 
 from ._binding import (  # noqa: F401
@@ -14,6 +15,7 @@ from ._binding import (  # noqa: F401
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_workspace_bytes,
+    attn_merge,
     lib,
     library_path,
     make_problem,

@@ -18,8 +18,10 @@ ABI_VERSION = 1
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_fwd_workspace_bytes",
-            "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error", "attn_abi_version")
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_merge",
+            "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
+            "attn_abi_version")
+MERGE_MAX_PARTS = 8
 BWD_PASSES = {"all": "attn_bwd", "preprocess": "attn_bwd_preprocess", "dkdv": "attn_bwd_dkdv", "dq": "attn_bwd_dq"}
 
 
@@ -78,6 +80,8 @@ def lib():
         for name in BWD_PASSES.values():
             getattr(L, name).argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             getattr(L, name).restype = ctypes.c_int
+        L.attn_merge.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
+        L.attn_merge.restype = ctypes.c_int
         L.attn_fwd_workspace_bytes.argtypes = [pp]
         L.attn_fwd_workspace_bytes.restype = sz
         L.attn_bwd_workspace_bytes.argtypes = [pp]
@@ -235,3 +239,58 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
         if st != 0:
             _raise(st)
     return dq, dk, dv
+
+
+def merge_problem(o_like, cu_seqlens_q=None, max_seqlen_q=None):
+    """The query-side problem attn_merge reads: dense O [B,Sq,Hq,D] or packed O [Tq,Hq,D] (cu_seqlens_q
+    marks the packed layout; the merge does not read it)."""
+    packed = cu_seqlens_q is not None
+    p = AttnProblem()
+    p.abi_version = ABI_VERSION
+    p.dtype = _dtype_code(o_like)
+    p.heads_q = o_like.shape[-2]
+    p.heads_kv = o_like.shape[-2]
+    p.head_dim = o_like.shape[-1]
+    p.scale = 1.0
+    if packed:
+        p.batch = cu_seqlens_q.numel() - 1
+        p.total_q = o_like.shape[0]
+        p.cu_seqlens_q = cu_seqlens_q.data_ptr()
+        p.max_seqlen_q = int(max_seqlen_q) if max_seqlen_q is not None else 0
+    else:
+        p.batch = o_like.shape[0]
+        p.max_seqlen_q = o_like.shape[1]
+    p.o_stride[:] = _strides(o_like, packed)
+    return p
+
+
+def attn_merge(o_parts, lse_parts, cu_seqlens_q=None, max_seqlen_q=None, out=None, lse=None, stream=None):
+    """Merge per-chunk forward results of the same queries over disjoint key sets (attn_merge).
+
+    o_parts: up to MERGE_MAX_PARTS tensors with one layout (dense [B,Sq,Hq,D] or packed [Tq,Hq,D]);
+    lse_parts: their fp32 Stats ([B,Hq,Sq] or [Tq,Hq]). ``out`` / ``lse`` may be one of the parts
+    (in-place). Returns (O, LSE).
+    """
+    import torch
+    o_parts, lse_parts = list(o_parts), list(lse_parts)
+    if not o_parts or len(o_parts) != len(lse_parts):
+        raise ValueError("o_parts and lse_parts must be non-empty and of equal length")
+    _check_device(*o_parts, *lse_parts, out, lse, cu_seqlens_q)
+    ref = o_parts[0]
+    for x in o_parts:
+        if x.shape != ref.shape or x.stride() != ref.stride() or x.dtype != ref.dtype:
+            raise ValueError("all parts of O must share shape, strides and dtype")
+    if out is None:
+        out = torch.empty_like(ref)
+    if out.stride() != ref.stride():
+        raise ValueError("out must have the parts' strides")
+    if lse is None:
+        lse = torch.empty_like(lse_parts[0])
+    p = merge_problem(ref, cu_seqlens_q, max_seqlen_q)
+    n = len(o_parts)
+    oa = (ctypes.c_void_p * n)(*[x.data_ptr() for x in o_parts])
+    la = (ctypes.c_void_p * n)(*[x.data_ptr() for x in lse_parts])
+    st = lib().attn_merge(ctypes.byref(p), n, oa, la, _ptr(out), _ptr(lse), _stream(stream))
+    if st != 0:
+        _raise(st)
+    return out, lse

@@ -378,3 +378,78 @@ attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k,
 }
 
 }  // extern "C"
+
+extern "C" {
+
+// Merge of per-chunk results (include/attn.h). Only the query side of the problem is validated.
+attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* const* o_parts,
+                         const float* const* lse_parts, void* o, float* lse, void* stream) {
+  try {
+    if (!p) return fail(ATTN_E_INVALID, "problem pointer is NULL");
+    if (p->abi_version != ATTN_ABI_VERSION)
+      return fail(ATTN_E_UNSUPPORTED, "abi_version %d is not this library's %d", p->abi_version, ATTN_ABI_VERSION);
+    if (p->dtype != ATTN_BF16 && p->dtype != ATTN_FP16)
+      return fail(ATTN_E_UNSUPPORTED, "dtype %d is not bf16 (0) or fp16 (1)", p->dtype);
+    if (p->batch < 0) return fail(ATTN_E_INVALID, "batch %d < 0", p->batch);
+    if (p->heads_q < 1) return fail(ATTN_E_INVALID, "heads_q must be >= 1");
+    if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256 && p->head_dim != 512)
+      return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not built (64, 128, 256, 512)", p->head_dim);
+    if (p->max_seqlen_q < 0) return fail(ATTN_E_INVALID, "negative max_seqlen_q");
+    if (n_parts < 1 || n_parts > ATTN_MERGE_MAX_PARTS)
+      return fail(ATTN_E_INVALID, "n_parts %d is not in [1, %d]", n_parts, ATTN_MERGE_MAX_PARTS);
+    if (!o_parts || !lse_parts) return fail(ATTN_E_INVALID, "o_parts or lse_parts array is NULL");
+    Info in;
+    in.packed = p->cu_seqlens_q != nullptr;
+    if (in.packed && (p->total_q < 0 || p->total_q > INT32_MAX))
+      return fail(ATTN_E_INVALID, "total_q %lld out of range", (long long)p->total_q);
+    in.nq = in.packed ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
+    in.nkv = 0;
+    for (int i = 0; i < (in.packed ? 2 : 3); ++i) {
+      if (p->o_stride[i] < 0) return fail(ATTN_E_INVALID, "o_stride[%d] is negative", i);
+      if (p->o_stride[i] % 8)
+        return fail(ATTN_E_ALIGN, "o_stride[%d] = %lld is not a multiple of 8 elements (16 bytes)", i,
+                    (long long)p->o_stride[i]);
+    }
+    const Extent eo = ext_q(p, o, p->o_stride, false, in), el = ext_lse(p, lse, in);
+    attn_status_t st = check_ptr(o, eo, "o");
+    if (st) return st;
+    if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
+    if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
+    if (overlaps(eo, el)) return fail(ATTN_E_OVERLAP, "o overlaps lse");
+    for (int k = 0; k < n_parts; ++k) {
+      const Extent ok = ext_q(p, o_parts[k], p->o_stride, false, in), lk = ext_lse(p, lse_parts[k], in);
+      if ((st = check_ptr(o_parts[k], ok, "o_parts[k]"))) return st;
+      if (!lk.empty() && !lse_parts[k]) return fail(ATTN_E_INVALID, "lse_parts[%d] is NULL", k);
+      if (!lk.empty() && !aligned(lse_parts[k], 4)) return fail(ATTN_E_ALIGN, "lse_parts[%d] is not 4-byte aligned", k);
+      // an output may be exactly one of the parts (same base and layout); any other overlap is refused
+      if (overlaps(eo, ok) && o != o_parts[k]) return fail(ATTN_E_OVERLAP, "o partially overlaps o_parts[%d]", k);
+      if (overlaps(el, lk) && lse != lse_parts[k])
+        return fail(ATTN_E_OVERLAP, "lse partially overlaps lse_parts[%d]", k);
+      if (overlaps(eo, lk)) return fail(ATTN_E_OVERLAP, "o overlaps lse_parts[%d]", k);
+      if (overlaps(el, ok)) return fail(ATTN_E_OVERLAP, "lse overlaps o_parts[%d]", k);
+    }
+    if (in.nq <= 0 || (!in.packed && p->batch == 0)) return ATTN_OK;
+
+    sdpa::MergeArgs a{};
+    for (int k = 0; k < n_parts; ++k) {
+      a.o_parts[k] = o_parts[k];
+      a.lse_parts[k] = lse_parts[k];
+    }
+    a.o = o;
+    a.lse = lse;
+    a.n_parts = n_parts;
+    a.hq = p->heads_q;
+    a.sq = p->max_seqlen_q;
+    a.packed = in.packed ? 1 : 0;
+    a.nrows = in.nq * p->heads_q;
+    a.ao = addr(p->o_stride, in.packed);
+    a.alse = lse_addr(p, in.packed);
+    const int e = sdpa::launch_merge(p->dtype, p->head_dim, a, stream);
+    if (e) return fail(ATTN_E_HIP, "merge launch: %s", hipGetErrorString((hipError_t)e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_INVALID, "internal error");
+  }
+}
+
+}  // extern "C"

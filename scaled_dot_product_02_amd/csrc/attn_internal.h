@@ -56,12 +56,27 @@ struct BwdArgs {
   int32_t n_kvtiles;  // ceil(skv / key tile) of the dK/dV kernel
 };
 
+// Merge of per-chunk results (attn_merge): nrows = query rows * hq independent (row, head) pairs.
+constexpr int kMergeMaxParts = 8;
+struct MergeArgs {
+  const void* o_parts[kMergeMaxParts];
+  const float* lse_parts[kMergeMaxParts];
+  void* o;
+  float* lse;
+  int32_t n_parts;
+  int32_t hq, sq;     // sq: dense sequence length (unused for packed)
+  int32_t packed;
+  int64_t nrows;      // tokens * hq
+  TensorAddr ao, alse;
+};
+
 // Launchers (attn_kernels.hip). Return hipError_t as int.
 int launch_validate_cu(const AttnShape& s, void* stream);
 int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream);
 // Backward passes selected by bit: 1 = preprocess, 2 = dK/dV pass, 4 = dQ pass.
 enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassAll = 7 };
 int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream);
+int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
 int fwd_query_tile(int head_dim);
 int bwd_key_tile(int head_dim);
 int bwd_query_tile(int head_dim);

@@ -234,3 +234,46 @@ def test_problem_struct_layout():
     assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24
     assert B.AttnProblem.cu_seqlens_q.offset == 40
     assert B.AttnProblem.q_stride.offset == 72
+
+
+# ---- attn_merge (validation only: every call below returns before a launch)
+def merge(L, p, n=2, o_parts=None, lse_parts=None, o=O, lse=LSE):
+    o_parts = o_parts if o_parts is not None else [Q, K][:n] + [V] * max(0, n - 2)
+    lse_parts = lse_parts if lse_parts is not None else [DO + i * (1 << 24) for i in range(n)]
+    oa = (ctypes.c_void_p * max(1, n))(*o_parts[:n]) if n > 0 else None
+    la = (ctypes.c_void_p * max(1, n))(*lse_parts[:n]) if n > 0 else None
+    return L.attn_merge(ctypes.byref(p) if p is not None else None, n, oa, la, o, lse, None)
+
+
+def test_merge_declines(L):
+    p = dense_problem()
+    expect(L, merge(L, None), INVALID, "NULL")
+    expect(L, merge(L, p, n=0), INVALID, "n_parts")
+    expect(L, merge(L, p, n=9), INVALID, "n_parts")
+    bad = dense_problem(d=96)
+    expect(L, merge(L, bad), UNSUPPORTED, "head_dim")
+    bad = dense_problem()
+    bad.dtype = 5
+    expect(L, merge(L, bad), UNSUPPORTED, "dtype")
+    al = dense_problem()
+    al.o_stride[1] = 132
+    expect(L, merge(L, al), ALIGN, "o_stride")
+    expect(L, merge(L, p, o=O + 8), ALIGN, "o")
+    expect(L, merge(L, p, lse=LSE + 2), ALIGN, "lse")
+    expect(L, merge(L, p, o_parts=[Q + 8, K]), ALIGN, "o_parts")
+
+
+def test_merge_overlap_rules(L):
+    p = dense_problem()
+    expect(L, merge(L, p, o=Q + 4096), OVERLAP, "partially overlaps o_parts")
+    expect(L, merge(L, p, lse=DO + 64), OVERLAP, "partially overlaps lse_parts")
+    expect(L, merge(L, p, o=DO), OVERLAP, "o overlaps lse_parts")
+    expect(L, merge(L, p, lse=Q + 64), OVERLAP, "lse overlaps o_parts")
+    expect(L, merge(L, p, lse=O + 64), OVERLAP, "o overlaps lse")
+
+
+def test_merge_empty_is_a_no_op(L):
+    assert merge(L, dense_problem(b=0)) == OK
+    assert merge(L, dense_problem(sq=0, skv=0)) == OK
+    # exact aliasing of an output with a part is accepted (nothing to launch here)
+    assert merge(L, dense_problem(b=0), o=Q, lse=DO) == OK

@@ -21,19 +21,26 @@ import torch
 from .sdpa_ref import MASK_NONE, MASK_CAUSAL_TL, MASK_CAUSAL_BR
 
 
-def _allowed(sq, skv, mask):
+def _allowed(sq, skv, mask, window_left=-1):
     i = torch.arange(sq)[:, None]
     j = torch.arange(skv)[None, :]
     if mask == MASK_NONE:
+        if window_left >= 0:
+            raise ValueError("a sliding window needs a causal mask")
         return torch.ones(sq, skv, dtype=torch.bool)
     if mask == MASK_CAUSAL_TL:
-        return j <= i
-    if mask == MASK_CAUSAL_BR:
-        return j <= i + (skv - sq)
-    raise ValueError(mask)
+        delta = 0
+    elif mask == MASK_CAUSAL_BR:
+        delta = skv - sq
+    else:
+        raise ValueError(mask)
+    allow = j <= i + delta
+    if window_left >= 0:
+        allow = allow & (j >= i + delta - window_left)
+    return allow
 
 
-def floor_head(q, k, v, do, scale, mask, dtype):
+def floor_head(q, k, v, do, scale, mask, dtype, window_left=-1):
     """One (sequence, q-head) in dtype. Inputs are torch tensors of ``dtype``.
 
     Returns fp32 tensors O, LSE, dQ, dK, dV (their values are dtype-representable
@@ -44,7 +51,7 @@ def floor_head(q, k, v, do, scale, mask, dtype):
 
     qf, kf, vf, dof = (t.to(torch.float32) for t in (q, k, v, do))
     sq, skv = qf.shape[0], kf.shape[0]
-    allow = _allowed(sq, skv, mask)
+    allow = _allowed(sq, skv, mask, window_left)
     s = rnd(scale * (qf @ kf.T))
     s = torch.where(allow, s, torch.tensor(float("-inf")))
     live = allow.any(dim=1)
@@ -62,7 +69,7 @@ def floor_head(q, k, v, do, scale, mask, dtype):
     return o, lse, dq, dk, dv
 
 
-def floor_units(q, k, v, do, mask, scale, dtype, units, cu_seqlens_q=None, cu_seqlens_kv=None):
+def floor_units(q, k, v, do, mask, scale, dtype, units, cu_seqlens_q=None, cu_seqlens_kv=None, window_left=-1):
     """Floor over the (sequence b, kv-head g) units; returns dicts keyed by unit.
 
     Each entry holds O and LSE for every q-head of the group ([grp, sq, D] and
@@ -81,7 +88,8 @@ def floor_units(q, k, v, do, mask, scale, dtype, units, cu_seqlens_q=None, cu_se
         os_, ls_, dqs = [], [], []
         dk_acc = dv_acc = None
         for h in range(g * grp, (g + 1) * grp):
-            o, lse, dq, dk, dv = floor_head(q[qs + (h,)], k[ks + (g,)], v[ks + (g,)], do[qs + (h,)], scale, mask, dtype)
+            o, lse, dq, dk, dv = floor_head(q[qs + (h,)], k[ks + (g,)], v[ks + (g,)], do[qs + (h,)], scale, mask, dtype,
+                                            window_left)
             os_.append(o)
             ls_.append(lse)
             dqs.append(dq)

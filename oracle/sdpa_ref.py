@@ -48,24 +48,33 @@ MASK_CAUSAL_TL = 1
 MASK_CAUSAL_BR = 2
 
 
-def allowed_pairs(sq, skv, mask):
+def allowed_pairs(sq, skv, mask, window_left=-1):
     """Boolean [sq, skv]: which (query, key) pairs the mask admits.
 
     [P1] Scope names the three masks; [P1] Approach describes the
-    bottom-right band (the causal diagonal aligned to the last key).
+    bottom-right band (the causal diagonal aligned to the last key). With
+    window_left = W >= 0 a causal mask also drops keys more than W before the
+    diagonal ([P1] Scope, sliding windows).
     """
     i = np.arange(sq)[:, None]
     j = np.arange(skv)[None, :]
     if mask == MASK_NONE:
+        if window_left >= 0:
+            raise ValueError("a sliding window needs a causal mask (it fixes the diagonal)")
         return np.ones((sq, skv), dtype=bool)
     if mask == MASK_CAUSAL_TL:
-        return j <= i
-    if mask == MASK_CAUSAL_BR:
-        return j <= i + (skv - sq)
-    raise ValueError(f"unknown mask {mask}")
+        delta = 0
+    elif mask == MASK_CAUSAL_BR:
+        delta = skv - sq
+    else:
+        raise ValueError(f"unknown mask {mask}")
+    allow = j <= i + delta
+    if window_left >= 0:
+        allow &= j >= i + delta - window_left
+    return allow
 
 
-def head_forward(q, k, v, scale, mask):
+def head_forward(q, k, v, scale, mask, window_left=-1):
     """One (sequence, q-head): returns O [sq, D], LSE [sq] (natural log), P [sq, skv].
 
     S = scale * q k^T; masked entries are -inf; LSE_i = log sum_j exp(S_ij)
@@ -75,7 +84,7 @@ def head_forward(q, k, v, scale, mask):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     sq, skv = q.shape[0], k.shape[0]
-    allow = allowed_pairs(sq, skv, mask)
+    allow = allowed_pairs(sq, skv, mask, window_left)
     s = np.where(allow, scale * (q @ k.T), -np.inf)
     live = allow.any(axis=1)
     lse = np.full(sq, -np.inf)
@@ -89,7 +98,7 @@ def head_forward(q, k, v, scale, mask):
     return o, lse, p
 
 
-def head_backward(q, k, v, do, scale, mask):
+def head_backward(q, k, v, do, scale, mask, window_left=-1):
     """One (sequence, q-head): returns dQ [sq, D], dK [skv, D], dV [skv, D].
 
     Gradients of the forward above with respect to q, k, v for the upstream
@@ -106,7 +115,7 @@ def head_backward(q, k, v, do, scale, mask):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
-    _, _, p = head_forward(q, k, v, scale, mask)
+    _, _, p = head_forward(q, k, v, scale, mask, window_left)
     dv = p.T @ do
     dp = do @ v.T
     dvec = (p * dp).sum(axis=1)
@@ -150,7 +159,7 @@ def _units(nseq, hkv, units):
     return [(b, g) for b in range(nseq) for g in range(hkv)] if units is None else list(units)
 
 
-def sdpa_fwd(q, k, v, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=None):
+def sdpa_fwd(q, k, v, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=None, window_left=-1):
     """Forward over a batch: returns O (float64, Q's layout) and LSE.
 
     ``units`` optionally restricts the work to (sequence b, kv-head g) pairs;
@@ -170,7 +179,7 @@ def sdpa_fwd(q, k, v, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=
     for b, g in _units(len(seqs), hkv, units):
         _, qi, ki = seqs[b]
         for h in range(g * grp, (g + 1) * grp):
-            oh, lh, _ = head_forward(q[qi + (h,)], k[ki + (g,)], v[ki + (g,)], scale, mask)
+            oh, lh, _ = head_forward(q[qi + (h,)], k[ki + (g,)], v[ki + (g,)], scale, mask, window_left)
             o[qi + (h,)] = oh
             if packed:
                 lse[qi + (h,)] = lh
@@ -179,7 +188,7 @@ def sdpa_fwd(q, k, v, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=
     return o, lse
 
 
-def sdpa_bwd(q, k, v, do, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=None):
+def sdpa_bwd(q, k, v, do, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=None, window_left=-1):
     """Backward over a batch: returns dQ, dK, dV (float64, layouts of Q, K, V).
 
     dK and dV of kv-head g sum the contributions of every q-head in g's group.
@@ -201,7 +210,8 @@ def sdpa_bwd(q, k, v, do, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, un
         dk_acc = np.zeros(k[ki + (g,)].shape)
         dv_acc = np.zeros(v[ki + (g,)].shape)
         for h in range(g * grp, (g + 1) * grp):
-            dqh, dkh, dvh = head_backward(q[qi + (h,)], k[ki + (g,)], v[ki + (g,)], do[qi + (h,)], scale, mask)
+            dqh, dkh, dvh = head_backward(q[qi + (h,)], k[ki + (g,)], v[ki + (g,)], do[qi + (h,)], scale, mask,
+                                          window_left)
             dq[qi + (h,)] = dqh
             dk_acc += dkh
             dv_acc += dvh
@@ -210,22 +220,30 @@ def sdpa_bwd(q, k, v, do, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, un
     return dq, dk, dv
 
 
-def count_allowed_pairs(seqlens_q, seqlens_kv, mask):
+def count_allowed_pairs(seqlens_q, seqlens_kv, mask, window_left=-1):
     """Number of allowed (query, key) pairs summed over sequences, for one head.
 
-    Closed forms of the masks above: none -> Sq*Skv; TL -> sum_i min(i+1, Skv);
-    BR -> sum_i clip(i + Skv - Sq + 1, 0, Skv).
+    Closed forms of the masks above: none -> Sq*Skv; causal with diagonal
+    delta (0 for TL, Skv - Sq for BR): row i sees keys max(0, i + delta - W)
+    .. min(Skv - 1, i + delta), i.e. clip(i + delta + 1, 0, Skv) keys less the
+    clip(i + delta - W, 0, Skv) keys before the window (W = -1: none).
     """
     total = 0
     for sq, skv in zip(seqlens_q, seqlens_kv):
         sq, skv = int(sq), int(skv)
         i = np.arange(sq, dtype=np.int64)
         if mask == MASK_NONE:
+            if window_left >= 0:
+                raise ValueError("a sliding window needs a causal mask (it fixes the diagonal)")
             total += sq * skv
-        elif mask == MASK_CAUSAL_TL:
-            total += int(np.clip(i + 1, 0, skv).sum())
+            continue
+        if mask == MASK_CAUSAL_TL:
+            delta = 0
         elif mask == MASK_CAUSAL_BR:
-            total += int(np.clip(i + skv - sq + 1, 0, skv).sum())
+            delta = skv - sq
         else:
             raise ValueError(f"unknown mask {mask}")
+        upto = np.clip(i + delta + 1, 0, skv)
+        before = np.clip(i + delta - window_left, 0, skv) if window_left >= 0 else 0
+        total += int(np.maximum(upto - before, 0).sum())
     return total

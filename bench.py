@@ -58,21 +58,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def allowed_pairs(lq, lk, mask):
-    """Allowed (query, key) pairs of one head, summed over sequences (closed forms)."""
+def allowed_pairs(lq, lk, mask, window_left=-1):
+    """Allowed (query, key) pairs of one head, summed over sequences (closed forms).
+
+    Causal with diagonal delta (0 TL, Skv - Sq BR): row i sees keys up to i + delta, and with a
+    sliding window W >= 0 only from i + delta - W on.
+    """
     total = 0
     for sq, skv in zip(lq, lk):
         if mask == "none":
             total += sq * skv
             continue
         delta = skv - sq if mask == "causal_br" else 0
-        # row i sees min(skv, max(0, i + delta + 1)) keys
-        lo = max(0, -delta)                 # first row with at least one key
-        full = max(lo, min(sq, skv - delta))  # rows i >= full see all skv keys
-        if full > lo:
-            a, b = lo + delta + 1, full - 1 + delta + 1
-            total += (a + b) * (full - lo) // 2
-        total += (sq - full) * skv
+
+        def upto(n):  # sum over rows i < n of min(skv, max(0, i + delta + 1)): keys at or below the diagonal
+            n = max(0, min(n, sq))
+            lo = max(0, -delta)                 # first row with at least one key
+            full = max(lo, min(n, skv - delta))  # rows i >= full see all skv keys
+            t = 0
+            if full > lo:
+                a, b = lo + delta + 1, full - 1 + delta + 1
+                t += (a + b) * (full - lo) // 2
+            t += max(0, n - full) * skv
+            return t
+        total += upto(sq)
+        if window_left >= 0:
+            # keys before the window: min(skv, max(0, i + delta - W)) for each row = the same sum with
+            # the diagonal moved down by W + 1
+            d2 = delta - window_left - 1
+            lo2 = max(0, -d2)
+            full2 = max(lo2, min(sq, skv - d2))
+            if full2 > lo2:
+                a, b = lo2 + d2 + 1, full2 - 1 + d2 + 1
+                total -= (a + b) * (full2 - lo2) // 2
+            total -= max(0, sq - full2) * skv
     return total
 
 
@@ -91,10 +110,11 @@ def cpu_baseline(w, x, budget_s=12.0, max_units=6):
     for unit in order[:max_units]:
         b, g = unit
         t0 = time.perf_counter()
-        sdpa_fwd(f64["q"], f64["k"], f64["v"], mask, w.scale, cu_q, cu_k, units=[unit])
-        sdpa_bwd(f64["q"], f64["k"], f64["v"], f64["do"], mask, w.scale, cu_q, cu_k, units=[unit])
+        sdpa_fwd(f64["q"], f64["k"], f64["v"], mask, w.scale, cu_q, cu_k, units=[unit], window_left=w.window_left)
+        sdpa_bwd(f64["q"], f64["k"], f64["v"], f64["do"], mask, w.scale, cu_q, cu_k, units=[unit],
+                 window_left=w.window_left)
         t_total += time.perf_counter() - t0
-        flops += 14.0 * w.d * grp * allowed_pairs([x["seqlens_q"][b]], [x["seqlens_kv"][b]], w.mask)
+        flops += 14.0 * w.d * grp * allowed_pairs([x["seqlens_q"][b]], [x["seqlens_kv"][b]], w.mask, w.window_left)
         done.append(unit)
         if t_total >= budget_s:
             break
@@ -116,12 +136,12 @@ def run(w, steps, warmup, want_events=True):
     dev = torch.device("cuda:0")
     x = make_inputs(w)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
-    kw = dict(mask=w.mask, scale=w.scale)
+    kw = dict(mask=w.mask, scale=w.scale, window_left=w.window_left)
     if w.packed:
         kw.update(cu_seqlens_q=x["cu_seqlens_q"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
                   max_seqlen_q=x["max_seqlen_q"], max_seqlen_kv=x["max_seqlen_kv"])
     p = sd.make_problem(q, k, v, q, w.mask, w.scale, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_kv"),
-                        x["max_seqlen_q"], x["max_seqlen_kv"])
+                        x["max_seqlen_q"], x["max_seqlen_kv"], w.window_left)
     o = torch.empty_like(q)
     lse_shape = (q.shape[0], q.shape[1]) if w.packed else (q.shape[0], q.shape[2], q.shape[1])
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
@@ -158,7 +178,7 @@ def run(w, steps, warmup, want_events=True):
     if evs:
         for j, n in enumerate(names):
             kern_ms[n] = sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
-    pairs = allowed_pairs(x["seqlens_q"], x["seqlens_kv"], w.mask) * w.hq
+    pairs = allowed_pairs(x["seqlens_q"], x["seqlens_kv"], w.mask, w.window_left) * w.hq
     return dict(x=x, ms_step=ms_step, kern_ms=kern_ms, pairs=pairs, nrows=p.total_q if w.packed else w.batch * w.sq)
 
 
@@ -260,7 +280,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch if not w.packed else len(r["x"]["seqlens_q"]),
                    "heads_q": w.hq, "heads_kv": w.hkv, "seq_q": w.sq or r["x"]["max_seqlen_q"],
                    "seq_kv": w.skv or r["x"]["max_seqlen_kv"], "head_dim": d, "mask": w.mask,
-                   "layout": "thd" if w.packed else "bshd", "allowed_pairs": pairs},
+                   "layout": "thd" if w.packed else "bshd", "window_left": w.window_left, "allowed_pairs": pairs},
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},

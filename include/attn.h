@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
@@ -59,7 +59,12 @@ typedef enum { ATTN_BF16 = 0, ATTN_FP16 = 1 } attn_dtype_t;
  *   ATTN_MASK_CAUSAL_BR  causal, bottom-right aligned: allowed iff j <= i + (Skv - Sq)
  * The bottom-right band is what a context-parallel rank holding the last Sq queries of a sequence
  * needs on its trimmed KV range (pull request 3527, section Approach). A query row with no allowed
- * key gets O = 0, LSE = -inf and a zero gradient. */
+ * key gets O = 0, LSE = -inf and a zero gradient.
+ * Sliding window (attn_problem_t.window_left = W >= 0, causal masks only; pull request 3527, section
+ * Scope: windows measured against the top-left or bottom-right diagonal): key j is allowed for query
+ * i iff i + delta - W <= j <= i + delta, with delta = 0 (TL) or Skv - Sq (BR): every query sees its
+ * diagonal key and the W keys before it. W = -1 means no window. A window with ATTN_MASK_NONE has no
+ * diagonal to measure from and is ATTN_E_UNSUPPORTED. */
 typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL_TL = 1, ATTN_MASK_CAUSAL_BR = 2 } attn_mask_t;
 
 /* One attention problem. All tensors have a contiguous head dimension (stride 1).
@@ -98,6 +103,8 @@ typedef struct attn_problem {
   int64_t k_stride[3];
   int64_t v_stride[3];
   int64_t o_stride[3];
+  int32_t window_left; /* sliding window below the causal diagonal (see above); -1 = none (ABI 2) */
+  int32_t reserved;    /* must be 0                                                   */
 } attn_problem_t;
 
 /* Workspace. Its first 256 bytes are a header whose int32 at offset 0 is the device error word:

@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsdpa02.so"
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
@@ -46,6 +46,8 @@ class AttnProblem(ctypes.Structure):
         ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3),
         ("o_stride", ctypes.c_int64 * 3),
+        ("window_left", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -122,7 +124,8 @@ def _check_device(*ts):
             raise ValueError("the head dimension must be contiguous (stride 1)")
 
 
-def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv):
+def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
+                 window_left=-1):
     packed = cu_seqlens_q is not None
     p = AttnProblem()
     p.abi_version = ABI_VERSION
@@ -150,6 +153,7 @@ def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_
     p.k_stride[:] = _strides(k, packed)
     p.v_stride[:] = _strides(v, packed)
     p.o_stride[:] = _strides(o_like, packed)
+    p.window_left = int(window_left)
     return p
 
 
@@ -181,7 +185,7 @@ def attn_bwd_workspace_bytes(p):
 
 
 def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
-             max_seqlen_kv=None, out=None, lse=None, workspace=None, stream=None):
+             max_seqlen_kv=None, out=None, lse=None, workspace=None, stream=None, window_left=-1):
     """Forward through the C-ABI. Returns (O, LSE).
 
     Dense q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]; packed q [Tq,Hq,D], k/v [Tkv,Hkv,D] with int32
@@ -195,7 +199,8 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
     if lse is None:
         shape = (q.shape[0], q.shape[1]) if packed else (q.shape[0], q.shape[2], q.shape[1])
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
-    p = make_problem(q, k, v, out, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv)
+    p = make_problem(q, k, v, out, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
+                     window_left)
     L = lib()
     need = L.attn_fwd_workspace_bytes(ctypes.byref(p))
     ws = _workspace(need, q.device, workspace)
@@ -208,7 +213,7 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
 
 def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None,
              max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
-             passes=("all",)):
+             passes=("all",), window_left=-1):
     """Backward through the C-ABI from the forward's O and LSE. Returns (dQ, dK, dV).
 
     dO must have O's strides; dQ/dK/dV are allocated with Q/K/V's shapes (contiguous) unless given.
@@ -227,7 +232,8 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
         dv = torch.empty_like(v, memory_format=torch.contiguous_format)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("dQ/dK/dV must have the strides of Q/K/V")
-    p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv)
+    p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
+                     window_left)
     L = lib()
     need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
     ws = _workspace(need, q.device, workspace)
@@ -261,6 +267,7 @@ def merge_problem(o_like, cu_seqlens_q=None, max_seqlen_q=None):
         p.batch = o_like.shape[0]
         p.max_seqlen_q = o_like.shape[1]
     p.o_stride[:] = _strides(o_like, packed)
+    p.window_left = -1
     return p
 
 

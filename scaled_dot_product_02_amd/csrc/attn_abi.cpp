@@ -85,6 +85,11 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (!isfinite(p->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
   if (!(p->scale > 0.f)) return fail(ATTN_E_UNSUPPORTED, "scale %g is not positive", (double)p->scale);
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
+  if (p->window_left < -1) return fail(ATTN_E_INVALID, "window_left %d < -1", p->window_left);
+  if (p->window_left >= 0 && p->mask == ATTN_MASK_NONE)
+    return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
+                p->window_left);
+  if (p->reserved != 0) return fail(ATTN_E_INVALID, "reserved field is %d, must be 0", p->reserved);
   const bool packed = p->cu_seqlens_q != nullptr;
   if (packed != (p->cu_seqlens_kv != nullptr))
     return fail(ATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_kv must both be set (packed) or both be NULL");
@@ -149,6 +154,7 @@ sdpa::AttnShape make_shape(const attn_problem_t* p, const Info& in, void* ws, in
   s.sq = p->max_seqlen_q;
   s.skv = p->max_seqlen_kv;
   s.mask = p->mask;
+  s.wl = p->window_left;
   s.n_qtiles = (p->max_seqlen_q + qtile - 1) / qtile;
   s.total_q = in.packed ? p->total_q : 0;
   s.total_kv = in.packed ? p->total_kv : 0;

@@ -21,6 +21,7 @@ struct AttnShape {
   int32_t batch, hq, hkv, group;  // group = hq / hkv
   int32_t sq, skv;                // dense lengths, or the host-side maxima for packed batches
   int32_t mask;                   // attn_mask_t
+  int32_t wl;                     // sliding window below the diagonal, -1 = none (causal masks only)
   int32_t n_qtiles;               // ceil(sq / query tile) of the launched kernel
   int64_t total_q, total_kv;      // packed token counts (for NaN fill on device errors)
   float scale;                    // softmax scale

@@ -239,6 +239,8 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
   const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BM + delta) : sq.skv;
   const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // first key tile inside some row's sliding window (0 without a window)
+  const int j0 = s.wl >= 0 ? max(0, q0 + delta - s.wl) / BN : 0;
 
   const us* qg = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
   const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
@@ -277,15 +279,17 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   int vkey[2];
 #pragma unroll
   for (int cp = 0; cp < 2; ++cp) vkey[cp] = (sw_key<D>(8 * cp + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3;
-  if (n_tiles > 0) issue(0, 0);
-  for (int j = 0; j < n_tiles; ++j) {
+  if (j0 < n_tiles) issue(j0, j0 & 1);
+  for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
     const int sb = (j & 1) * 4 * TILE;  // stage, bytes; K tile at sb, V tile at sb + 2*TILE
     const int kv0 = j * BN;
     if (s.mask != 0 && kv0 > qw0 + 31 + delta) continue;  // tile fully masked for this wave
-    const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta);
+    if (s.wl >= 0 && kv0 + BN - 1 < qw0 + delta - s.wl) continue;  // tile before this wave's windows
+    const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta) ||
+                           (s.wl >= 0 && kv0 < qw0 + 31 + delta - s.wl);
 
     // per-tile byte bases: the stage and row parts never touch the swizzled chunk bits, so each read
     // below is one XOR with a constant (plus an immediate offset)
@@ -314,11 +318,13 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
     float mt = -__builtin_inff();
     if (need_mask) {
       const int lim = min(sq.skv - 1, s.mask == 0 ? sq.skv : qi + delta) - kv0 - 4 * hh;
+      const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);  // window start
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int jr = 0; jr < 16; ++jr) {
-          const float x = 32 * kb + 8 * (jr >> 2) + (jr & 3) <= lim ? sacc[kb][jr] : -__builtin_inff();
+          const int off = 32 * kb + 8 * (jr >> 2) + (jr & 3);
+          const float x = off <= lim && off >= lo ? sacc[kb][jr] : -__builtin_inff();
           sacc[kb][jr] = x;
           mt = fmaxf(mt, x);
         }
@@ -428,6 +434,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
   const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BM + delta) : sq.skv;
   const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // first key tile inside some row's sliding window (0 without a window)
+  const int j0 = s.wl >= 0 ? max(0, q0 + delta - s.wl) / BN : 0;
 
   const us* qg = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;
   const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
@@ -466,15 +474,16 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   int vkey[2];
 #pragma unroll
   for (int cp = 0; cp < 2; ++cp) vkey[cp] = (sw_key<D>(8 * cp + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3;
-  if (n_tiles > 0) issue(0, 0);
-  for (int j = 0; j < n_tiles; ++j) {
+  if (j0 < n_tiles) issue(j0, j0 & 1);
+  for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
     const us* ks = smem + (j & 1) * 2 * TILE;
     const us* vs = ks + TILE;
     const int kv0 = j * BN;
-    const bool active = s.mask == 0 || kv0 <= qw0 + 31 + delta;  // same for both waves of a pair
+    const bool active = (s.mask == 0 || kv0 <= qw0 + 31 + delta) &&
+                        (s.wl < 0 || kv0 + BN - 1 >= qw0 + delta - s.wl);  // same for both waves of a pair
     const int kx = opaque(kkey), vx0 = opaque(vkey[0]), vx1 = opaque(vkey[1]);
     v16f sacc = v16f{};
     if (active) {
@@ -500,10 +509,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
     // Branch-free mask (a per-element branch here doubles the live S values and spills): key
     // kv0 + 8(jr/4) + 4hh + jr%4 is allowed iff its offset 8(jr/4) + jr%4 <= lim - kv0 - 4hh.
     const int lim = (s.mask != 0 ? min(sq.skv - 1, qi + delta) : sq.skv - 1) - kv0 - 4 * hh;
+    const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);  // window start
     float mt = -__builtin_inff();
 #pragma unroll
     for (int jr = 0; jr < 16; ++jr) {
-      const float x = (8 * (jr >> 2) + (jr & 3) <= lim) ? sacc[jr] : -__builtin_inff();
+      const int off = 8 * (jr >> 2) + (jr & 3);
+      const float x = (off <= lim && off >= lo) ? sacc[jr] : -__builtin_inff();
       sacc[jr] = x;
       mt = fmaxf(mt, x);
     }
@@ -641,7 +652,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
   const int q_lo = s.mask != 0 ? max(0, k0 - delta) : 0;
   const int qt0 = q_lo / BQ;
-  const int nq = max(0, (sq.sq + BQ - 1) / BQ - qt0);
+  // with a sliding window, rows past k0 + BKV - 1 - delta + W see none of these keys
+  const int q_hi = s.wl >= 0 ? k0 + BKV - 1 - delta + s.wl : sq.sq - 1;
+  const int nq = q_hi < 0 ? 0 : max(0, min((sq.sq + BQ - 1) / BQ, q_hi / BQ + 1) - qt0);
   const int n_it = nq * s.group;
 
   const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
@@ -703,7 +716,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
     if (kw0 >= sq.skv) continue;
     if (s.mask != 0 && qs0 + BQ - 1 + delta < kw0) continue;  // no row of the tile sees these keys
-    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1);
+    if (s.wl >= 0 && qs0 + delta - s.wl > kw0 + KW - 1) continue;  // every row's window starts later
+    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1) ||
+                           (s.wl >= 0 && qs0 + BQ - 1 + delta - s.wl > kw0);
 
     v4f sv[2][KB], dp[2][KB];
 #pragma unroll
@@ -736,7 +751,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int q = ql + 16 * qb + i;
             const int key = kl + 16 * kb;
-            const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
+            const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta) &&
+                             (s.wl < 0 || key >= q + delta - s.wl);
             sv[qb][kb][i] = ok ? sv[qb][kb][i] : -__builtin_inff();  // exp2 -> exactly 0
           }
     }
@@ -823,6 +839,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
   const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BMQ + delta) : sq.skv;
   const int n_tiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+  // first key tile inside some row's sliding window (0 without a window)
+  const int j0 = s.wl >= 0 ? max(0, q0 + delta - s.wl) / BK : 0;
   const int qw0 = q0 + w * QW;
   const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
 
@@ -861,8 +879,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
-  if (n_tiles > 0) issue(0, 0);
-  for (int j = 0; j < n_tiles; ++j) {
+  if (j0 < n_tiles) issue(j0, j0 & 1);
+  for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
@@ -871,7 +889,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     const us* vs = ks + KTILE;
     const int kv0 = j * BK;
     if (s.mask != 0 && kv0 > qw0 + QW - 1 + delta) continue;
-    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta);
+    if (s.wl >= 0 && kv0 + BK - 1 < qw0 + delta - s.wl) continue;  // tile before this wave's windows
+    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta) ||
+                           (s.wl >= 0 && kv0 < qw0 + QW - 1 + delta - s.wl);
 
     v4f st[2][QB], dpt[2][QB];
 #pragma unroll
@@ -908,7 +928,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) {
             const int q = qw0 + 16 * qb + l16;
             const int key = kv0 + 16 * kb + 4 * G + i;
-            const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta);
+            const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta) && (s.wl < 0 || key >= q + delta - s.wl);
             st[kb][qb][i] = ok ? st[kb][qb][i] : 0.f;
           }
     }
@@ -986,7 +1006,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
   const int q_lo = s.mask != 0 ? max(0, k0 - delta) : 0;
   const int qt0 = q_lo / BQ;
-  const int nq = max(0, (sq.sq + BQ - 1) / BQ - qt0);
+  // with a sliding window, rows past k0 + BKV - 1 - delta + W see none of these keys
+  const int q_hi = s.wl >= 0 ? k0 + BKV - 1 - delta + s.wl : sq.sq - 1;
+  const int nq = q_hi < 0 ? 0 : max(0, min((sq.sq + BQ - 1) / BQ, q_hi / BQ + 1) - qt0);
   const int n_it = nq * s.group;
 
   // role 0 keeps K, role 1 keeps V (B operands: key kw0 + l16, d = 32kk + 8G + t)
@@ -1038,8 +1060,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     const float* rss = l2s + 64;
     const int qs0 = qt_c * BQ;
     qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
-    const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0);
-    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1);
+    const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0) &&
+                        (s.wl < 0 || qs0 + delta - s.wl <= kw0 + KW - 1);
+    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1) ||
+                           (s.wl >= 0 && qs0 + BQ - 1 + delta - s.wl > kw0);
     v4f sv[2];  // role 0: S then P; role 1: dP then dS
     if (active) {
       const us* src = role == 0 ? qs : dos;
@@ -1061,7 +1085,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
             if (need_mask) {
               const int q = qs0 + 16 * qb + 4 * G + i;
               const int key = kw0 + l16;
-              const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta);
+              const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta) &&
+                             (s.wl < 0 || key >= q + delta - s.wl);
               p = ok ? p : 0.f;
             }
             sv[qb][i] = p;
@@ -1132,6 +1157,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
   const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BMQ + delta) : sq.skv;
   const int n_tiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+  // first key tile inside some row's sliding window (0 without a window)
+  const int j0 = s.wl >= 0 ? max(0, q0 + delta - s.wl) / BK : 0;
   const int qw0 = q0 + pr * QW;
   const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
 
@@ -1154,10 +1181,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   for (int dt = 0; dt < DH / 16; ++dt) dq[dt] = v4f{};
 
   const TileDma<D, BK, NDMA> dma(w, lane, a.ak.row, a.av.row);
-  // issue() is called for tiles 0, 1, 2, ... in order: running tile pointers
+  // issue() is called for tiles j0, j0 + 1, ... in order: running tile pointers
   const int64_t kstep = (int64_t)BK * a.ak.row, vstep = (int64_t)BK * a.av.row;
-  const us* k_ld = kg;
-  const us* v_ld = vg;
+  const us* k_ld = kg + j0 * kstep;
+  const us* v_ld = vg + j0 * vstep;
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
@@ -1172,8 +1199,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   float* mine = xch + w * 2 * 64 * 4;
   const float* other = xch + (w ^ 4) * 2 * 64 * 4;
 
-  if (n_tiles > 0) issue(0, 0);
-  for (int j = 0; j < n_tiles; ++j) {
+  if (j0 < n_tiles) issue(j0, j0 & 1);
+  for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
@@ -1181,8 +1208,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     const us* ks = smem + (j & 1) * 2 * KTILE;
     const us* vs = ks + KTILE;
     const int kv0 = j * BK;
-    const bool active = s.mask == 0 || kv0 <= qw0 + QW - 1 + delta;
-    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta);
+    const bool active = (s.mask == 0 || kv0 <= qw0 + QW - 1 + delta) && (s.wl < 0 || kv0 + BK - 1 >= qw0 + delta - s.wl);
+    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta) ||
+                           (s.wl >= 0 && kv0 < qw0 + QW - 1 + delta - s.wl);
     v4f st[2];  // S^T -> P (role 0) or dP^T (role 1): key kv0 + 16kb + 4G + i, query qw0 + l16
     if (active) {
       const us* src = role == 0 ? ks : vs;
@@ -1203,7 +1231,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
             if (need_mask) {
               const int q = qw0 + l16;
               const int key = kv0 + 16 * kb + 4 * G + i;
-              const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta);
+              const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta) && (s.wl < 0 || key >= q + delta - s.wl);
               p = ok ? p : 0.f;
             }
             st[kb][i] = p;

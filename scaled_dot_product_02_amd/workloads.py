@@ -44,6 +44,8 @@ class Workload:
     # explicit packed lengths (tests); overrides len_range when given
     seqlens: Optional[Tuple[int, ...]] = None
     seqlens_kv: Optional[Tuple[int, ...]] = None
+    # sliding window below the causal diagonal (keys i+delta-W .. i+delta); -1 = none
+    window_left: int = -1
     note: str = field(default="", compare=False)
 
     @property
@@ -72,6 +74,10 @@ WORKLOADS = {
                               mask="causal_br", seed=4, note="single-rank CP share: Sq4096 vs Skv16384 BR, D256 fp16"),
     "cp_share_d512": Workload("cp_share_d512", batch=1, hq=16, hkv=8, sq=4096, skv=16384, d=512, dtype="fp16",
                               mask="causal_br", seed=4, note="single-rank CP share: Sq4096 vs Skv16384 BR, D512 fp16"),
+    # a local (sliding-window) layer at D=256, the other half of the hybrid model pull request 3527 motivates
+    "window_d256": Workload("window_d256", batch=1, hq=16, hkv=8, sq=8192, skv=8192, d=256, dtype="bf16",
+                            mask="causal_tl", window_left=1023, seed=5,
+                            note="B1 Hq16/Hkv8 S8192 D256 bf16 causal with a 1024-key sliding window"),
 }
 
 
@@ -111,8 +117,8 @@ def make_inputs(w: Workload, with_do: bool = True):
 
 
 def small(name="small", *, batch=1, hq=2, hkv=2, sq=64, skv=64, d=64, dtype="bf16", mask="causal_tl", seed=0,
-          seqlens=None, seqlens_kv=None):
+          seqlens=None, seqlens_kv=None, window_left=-1):
     """A test-sized workload with the same recipe."""
     return Workload(name, batch=batch, hq=hq, hkv=hkv, sq=sq, skv=skv, d=d, dtype=dtype, mask=mask, seed=seed,
                     seqlens=tuple(seqlens) if seqlens is not None else None,
-                    seqlens_kv=tuple(seqlens_kv) if seqlens_kv is not None else None)
+                    seqlens_kv=tuple(seqlens_kv) if seqlens_kv is not None else None, window_left=window_left)

@@ -40,7 +40,7 @@ def gpu_run(w, x, backward=True, stream=None):
     """Forward (and backward) of workload w on cuda:0 through the C-ABI; returns CPU tensors."""
     dev = torch.device("cuda:0")
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
-    kw = dict(mask=w.mask, scale=w.scale)
+    kw = dict(mask=w.mask, scale=w.scale, window_left=w.window_left)
     if w.packed:
         kw.update(cu_seqlens_q=x["cu_seqlens_q"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
                   max_seqlen_q=x["max_seqlen_q"], max_seqlen_kv=x["max_seqlen_kv"])
@@ -113,11 +113,13 @@ def check_units(w, x, got, units, verbose=True):
     xin = {n: f64(x[n]) for n in ("q", "k", "v", "do")}
     cu_q = x["cu_seqlens_q"].numpy() if w.packed else None
     cu_k = x["cu_seqlens_kv"].numpy() if w.packed else None
-    ro, rl = sdpa_fwd(xin["q"], xin["k"], xin["v"], mask, w.scale, cu_q, cu_k, units=units)
-    rdq, rdk, rdv = sdpa_bwd(xin["q"], xin["k"], xin["v"], xin["do"], mask, w.scale, cu_q, cu_k, units=units)
+    ro, rl = sdpa_fwd(xin["q"], xin["k"], xin["v"], mask, w.scale, cu_q, cu_k, units=units,
+                      window_left=w.window_left)
+    rdq, rdk, rdv = sdpa_bwd(xin["q"], xin["k"], xin["v"], xin["do"], mask, w.scale, cu_q, cu_k, units=units,
+                             window_left=w.window_left)
     t1 = time.time()
     flo = oracle_floor.floor_units(x["q"], x["k"], x["v"], x["do"], mask, w.scale, w.torch_dtype, units,
-                                   x["cu_seqlens_q"], x["cu_seqlens_kv"])
+                                   x["cu_seqlens_q"], x["cu_seqlens_kv"], window_left=w.window_left)
     t2 = time.time()
     g64 = {n: f64(t) for n, t in got.items()}
     msgs, all_ok = [], True

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.attn_abi_version() == 1
+    assert L.attn_abi_version() == 2
     for code, name in B.STATUS.items():
         assert L.attn_status_str(code).decode() == name
     assert L.attn_status_str(42).decode() == "ATTN_E_UNKNOWN"
@@ -49,7 +49,8 @@ def test_version_and_status_strings(L):
 
 def dense_problem(b=2, sq=256, skv=256, hq=4, hkv=2, d=128, dtype=0, mask=1):
     p = B.AttnProblem()
-    p.abi_version = 1
+    p.abi_version = 2
+    p.window_left = -1  # no sliding window (ctypes zero-fills, and 0 is a window)
     p.dtype, p.mask, p.scale = dtype, mask, d ** -0.5
     p.batch, p.heads_q, p.heads_kv, p.head_dim = b, hq, hkv, d
     p.max_seqlen_q, p.max_seqlen_kv = sq, skv
@@ -93,7 +94,10 @@ def test_null_problem(L):
 
 
 @pytest.mark.parametrize("field,value,want,frag", [
-    ("abi_version", 2, UNSUPPORTED, "abi_version"),
+    ("abi_version", 1, UNSUPPORTED, "abi_version"),
+    ("abi_version", 3, UNSUPPORTED, "abi_version"),
+    ("window_left", -2, INVALID, "window_left"),
+    ("reserved", 1, INVALID, "reserved"),
     ("dtype", 7, UNSUPPORTED, "dtype"),
     ("mask", 3, UNSUPPORTED, "mask"),
     ("mask", -1, UNSUPPORTED, "mask"),
@@ -230,10 +234,22 @@ def test_binding_rejects_host_tensors(lib_path):
 
 
 def test_problem_struct_layout():
-    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3]
-    assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24
+    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3], window_left + reserved (int32)
+    assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24 + 8
     assert B.AttnProblem.cu_seqlens_q.offset == 40
     assert B.AttnProblem.q_stride.offset == 72
+    assert B.AttnProblem.window_left.offset == 168
+
+
+def test_window_needs_a_causal_mask(L):
+    p = dense_problem(mask=0)
+    p.window_left = 16
+    expect(L, fwd(L, p), UNSUPPORTED, "causal mask")
+    expect(L, bwd(L, p), UNSUPPORTED, "causal mask")
+    for mask in (1, 2):
+        p = dense_problem(b=0, mask=mask)
+        p.window_left = 0
+        assert fwd(L, p) == OK
 
 
 # ---- attn_merge (validation only: every call below returns before a launch)

@@ -77,6 +77,7 @@ FULL_UNITS = {
     "dense_d512": [(0, 1)],
     "cp_share_d256": [(0, 6)],
     "cp_share_d512": [(0, 3)],
+    "window_d256": [(0, 2)],
 }
 
 
@@ -94,4 +95,37 @@ def test_full_workload(name):
         lens = x["seqlens_q"]
         units = [(lens.index(max(lens)), 3), (lens.index(min(lens)), 0)]
     ok, msgs = check_units(w, x, got, units)
+    assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
+
+
+# Sliding windows (pull request 3527, section Scope): causal masks with a window W below the diagonal.
+def _window_cases():
+    cases = []
+    for d in (64, 128, 256, 512):
+        for dtype in ("bf16", "fp16"):
+            for mask in ("causal_tl", "causal_br"):
+                for wl in (0, 1, 37, 150):
+                    for sq, skv in (SHAPES if d == 128 else [(200, 200)]):
+                        cases.append((d, dtype, mask, wl, sq, skv))
+    return cases
+
+
+@pytest.mark.parametrize("case", _window_cases(), ids=lambda c: "d{}-{}-{}-w{}-{}x{}".format(*c))
+def test_window_sweep(case):
+    d, dtype, mask, wl, sq, skv = case
+    w = small(f"win_{d}_{dtype}_{mask}_{wl}", batch=2, hq=4, hkv=2, sq=sq, skv=skv, d=d, dtype=dtype, mask=mask,
+              seed=3 * d + wl + sq, window_left=wl)
+    ok, msgs = run_and_check(w)
+    assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("mask", ["causal_tl", "causal_br"])
+@pytest.mark.parametrize("wl", [0, 37])
+@pytest.mark.parametrize("lens", [0, 2])
+def test_window_packed(d, mask, wl, lens):
+    lq, lk = THD_CASES[lens]
+    w = small(f"thdwin_{d}_{mask}_{wl}_{lens}", hq=4, hkv=2, d=d, dtype="bf16", mask=mask, seed=11 + lens,
+              seqlens=lq, seqlens_kv=lk, window_left=wl)
+    ok, msgs = run_and_check(w)
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))

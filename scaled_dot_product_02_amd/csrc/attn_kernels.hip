@@ -816,7 +816,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 template <int D, int QB, int MINW, typename T>
 __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int NW = 4, QW = 16 * QB, BMQ = NW * QW, BK = 32, CH = D / 8;
+  // key tiles of BK = 64 (D <= 128) or 32 keys, processed as 32-key halves: a larger tile halves the
+  // barriers, waits and copy issues per key at the same register use
+  constexpr int NW = 4, QW = 16 * QB, BMQ = NW * QW, BK = D <= 128 ? 64 : 32, KH = BK / 32, CH = D / 8;
   constexpr int KTILE = BK * D;
   constexpr int NDMA = KTILE * 2 / 1024 / NW;
   static_assert(NDMA >= 1, "key tile must split over 4 waves");
@@ -884,13 +886,15 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+#pragma unroll
+   for (int kh = 0; kh < KH; ++kh) {  // 32-key half of the tile
     const int rx = opaque(rkey), tx = opaque(tkey);
-    const us* ks = smem + (j & 1) * 2 * KTILE;
+    const us* ks = smem + (j & 1) * 2 * KTILE + 32 * kh * D;
     const us* vs = ks + KTILE;
-    const int kv0 = j * BK;
+    const int kv0 = j * BK + 32 * kh;
     if (s.mask != 0 && kv0 > qw0 + QW - 1 + delta) continue;
-    if (s.wl >= 0 && kv0 + BK - 1 < qw0 + delta - s.wl) continue;  // tile before this wave's windows
-    const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta) ||
+    if (s.wl >= 0 && kv0 + 31 < qw0 + delta - s.wl) continue;  // keys before this wave's windows
+    const bool need_mask = (kv0 + 32 > sq.skv) || (s.mask != 0 && kv0 + 31 > qw0 + delta) ||
                            (s.wl >= 0 && kv0 < qw0 + QW - 1 + delta - s.wl);
 
     v4f st[2][QB], dpt[2][QB];
@@ -949,6 +953,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) dq[qb][dt] = Elem<T>::mma16(dsa[qb], Elem<T>::cast(kbt), dq[qb][dt]);
     }
+   }
   }
 
   T* dqp = (T*)a.dq + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head;

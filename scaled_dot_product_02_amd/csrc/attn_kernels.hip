@@ -627,7 +627,7 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 template <int D, int KB, int MINW, typename T>
 __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NW = 4, KW = 16 * KB, BKV = NW * KW, BQ = 32, CH = D / 8;
+  constexpr int NW = 4, KW = 16 * KB, BKV = NW * KW, BQ = D <= 128 ? 64 : 32, QH = BQ / 32, CH = D / 8;
   constexpr int QTILE = BQ * D;
   constexpr int NDMA = QTILE * 2 / 1024 / NW;
   static_assert(NDMA >= 1, "query tile must split over 4 waves");
@@ -709,17 +709,21 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
     if (it + 1 < n_it) issue((it + 1) & 1);
     const int sb = (it & 1) * STAGE;
-    const int rb = opaque(2 * (rrow + rkey)) + 2 * sb, tb = opaque(2 * (trow + tkey)) + 2 * sb;  // bytes
-    const float* l2s = reinterpret_cast<const float*>(smem + sb + 2 * QTILE);
-    const float* rss = l2s + 64;
     const int qs0 = qt_c * BQ;
     qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
     if (kw0 >= sq.skv) continue;
-    if (s.mask != 0 && qs0 + BQ - 1 + delta < kw0) continue;  // no row of the tile sees these keys
-    if (s.wl >= 0 && qs0 + delta - s.wl > kw0 + KW - 1) continue;  // every row's window starts later
-    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1) ||
-                           (s.wl >= 0 && qs0 + BQ - 1 + delta - s.wl > kw0);
-
+#pragma unroll
+   for (int qh = 0; qh < QH; ++qh) {  // 32-row half of the tile
+    const int qs = qs0 + 32 * qh;
+    if (qs >= sq.sq) continue;
+    if (s.mask != 0 && qs + 31 + delta < kw0) continue;  // no row of the half sees these keys
+    if (s.wl >= 0 && qs + delta - s.wl > kw0 + KW - 1) continue;  // every row's window starts later
+    const bool need_mask = (qs + 32 > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs + delta < kw0 + KW - 1) ||
+                           (s.wl >= 0 && qs + 31 + delta - s.wl > kw0);
+    const int hb = 2 * sb + 64 * D * qh;  // byte offset of the half's first row
+    const int rb = opaque(2 * (rrow + rkey)) + hb, tb = opaque(2 * (trow + tkey)) + hb;
+    const float* l2s = reinterpret_cast<const float*>(smem + sb + 2 * QTILE) + 32 * qh;
+    const float* rss = l2s + 64;
     v4f sv[2][KB], dp[2][KB];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -742,7 +746,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     }
     if (need_mask) {  // one branch per tile (a test inside the unrolled loop branches per element)
       // (opaque: the index arithmetic stays inside the branch instead of being hoisted onto every tile)
-      const int ql = opaque(qs0 + 4 * G), kl = opaque(kw0 + l16);
+      const int ql = opaque(qs + 4 * G), kl = opaque(kw0 + l16);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -788,6 +792,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
         dk[kb][dt] = Elem<T>::mma16(sa[kb], Elem<T>::cast(qbt), dk[kb][dt]);
       }
     }
+   }
   }
 
   T* dkp = (T*)a.dk + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;

@@ -12,8 +12,11 @@ Sources (the pages, by title and section):
          checked against an independent float64 reference; coverage is
          square and rectangular shapes, causal / bottom-right / no mask, GQA
          and MHA.
-       - Scope: the mask vocabulary no_mask / causal / causal_bottom_right,
-         symmetric head dims.
+       - Scope: the mask vocabulary no_mask / causal / causal_bottom_right;
+         head dims: the backward engine there is declared for any multiple
+         of 8 up to 512 (padded to its compiled width) and is held to
+         d_qk == d_v only by an engine flag, while the forward engine lists
+         the asymmetric pair (192, 128) natively.
   [P2] TransformerEngine pull request 3705 (FROST forward provider for
        context-parallel attention), section Description / Execution and
        supported scope: the forward returns fp32 Stats that are natural
@@ -35,9 +38,14 @@ Readings where the pages are silent (each also listed in the design notes):
     (neutral statistics; [P3] Description mentions neutral statistics for empty
     ragged ring blocks).
   * The scale multiplies Q K^T before masking and softmax.
+  * Head dims: Q and K share D_qk, V and O (hence dO, dV) have their own
+    D_v; nothing else depends on either (the scale is passed by value), so
+    the definition below is the same for any pair.  [P1 Scope; pinned by the
+    V-column split and zero-padding identities and by finite differences.]
 
-Layouts: dense Q/O/dO are [B, Sq, Hq, D], K/V [B, Skv, Hkv, D]; packed (THD)
-Q/O/dO are [Tq, Hq, D], K/V [Tkv, Hkv, D] with cu_seqlens of length B+1.
+Layouts: dense Q is [B, Sq, Hq, D_qk], O/dO [B, Sq, Hq, D_v], K [B, Skv, Hkv,
+D_qk], V [B, Skv, Hkv, D_v]; packed (THD) drops the batch axis and uses the
+token axis ([Tq, ...], [Tkv, ...]) with cu_seqlens of length B+1.
 LSE is [B, Hq, Sq] dense and [Tq, Hq] packed (token-major).
 """
 
@@ -75,7 +83,7 @@ def allowed_pairs(sq, skv, mask, window_left=-1):
 
 
 def head_forward(q, k, v, scale, mask, window_left=-1):
-    """One (sequence, q-head): returns O [sq, D], LSE [sq] (natural log), P [sq, skv].
+    """One (sequence, q-head): returns O [sq, D_v], LSE [sq] (natural log), P [sq, skv].
 
     S = scale * q k^T; masked entries are -inf; LSE_i = log sum_j exp(S_ij)
     (natural log, [P2] Description); P_ij = exp(S_ij - LSE_i); O = P v.
@@ -99,7 +107,7 @@ def head_forward(q, k, v, scale, mask, window_left=-1):
 
 
 def head_backward(q, k, v, do, scale, mask, window_left=-1):
-    """One (sequence, q-head): returns dQ [sq, D], dK [skv, D], dV [skv, D].
+    """One (sequence, q-head): returns dQ [sq, D_qk], dK [skv, D_qk], dV [skv, D_v].
 
     Gradients of the forward above with respect to q, k, v for the upstream
     gradient dO ([P1] Verification checks exactly these against float64):
@@ -146,8 +154,8 @@ def _check(q, k, v, packed):
     hq, hkv = q.shape[-2], k.shape[-2]
     if hq % hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    if v.shape != k.shape:
-        raise ValueError("K and V must have the same shape (symmetric head dim)")
+    if v.shape[:-1] != k.shape[:-1]:
+        raise ValueError("K and V must have the same tokens and heads")
     if q.shape[-1] != k.shape[-1]:
         raise ValueError("Q and K head dims differ")
     if (q.ndim != 3) if packed else (q.ndim != 4):
@@ -160,7 +168,7 @@ def _units(nseq, hkv, units):
 
 
 def sdpa_fwd(q, k, v, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=None, window_left=-1):
-    """Forward over a batch: returns O (float64, Q's layout) and LSE.
+    """Forward over a batch: returns O (float64, Q's layout with V's head dim) and LSE.
 
     ``units`` optionally restricts the work to (sequence b, kv-head g) pairs;
     every q-head of g's group is computed there, and all other outputs are NaN.
@@ -173,7 +181,7 @@ def sdpa_fwd(q, k, v, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, units=
     v = np.asarray(v, dtype=np.float64)
     hq, hkv = _check(q, k, v, packed)
     grp = hq // hkv
-    o = np.full(q.shape, np.nan)
+    o = np.full(q.shape[:-1] + v.shape[-1:], np.nan)
     lse = np.full(q.shape[:-1], np.nan) if packed else np.full((q.shape[0], hq, q.shape[1]), np.nan)
     seqs = list(_sequences(q, k, cu_seqlens_q, cu_seqlens_kv))
     for b, g in _units(len(seqs), hkv, units):
@@ -200,6 +208,8 @@ def sdpa_bwd(q, k, v, do, mask, scale, cu_seqlens_q=None, cu_seqlens_kv=None, un
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     hq, hkv = _check(q, k, v, packed)
+    if do.shape != q.shape[:-1] + v.shape[-1:]:
+        raise ValueError("dO must have O's shape (Q's layout with V's head dim)")
     grp = hq // hkv
     dq = np.full(q.shape, np.nan)
     dk = np.full(k.shape, np.nan)

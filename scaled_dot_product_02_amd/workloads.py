@@ -15,6 +15,7 @@ Recipe (identical for every consumer, GPU path and oracle alike):
   packed batches first draw their lengths: randint(lo, hi + 1, (nseq,))
   then Q, K, V, dO are drawn in that order as float32 N(0, 1) and rounded to
   the dtype (round to nearest even). Those dtype tensors are the inputs.
+  Q and K have head dim d; V and dO have d_v (= d unless set).
 """
 
 from dataclasses import dataclass, field
@@ -46,11 +47,17 @@ class Workload:
     seqlens_kv: Optional[Tuple[int, ...]] = None
     # sliding window below the causal diagonal (keys i+delta-W .. i+delta); -1 = none
     window_left: int = -1
+    # head dim of V, O, dO when it differs from d (the Q/K head dim); 0 = same as d
+    dv: int = 0
     note: str = field(default="", compare=False)
 
     @property
     def packed(self):
         return self.nseq > 0 or self.seqlens is not None
+
+    @property
+    def d_v(self):
+        return self.dv or self.d
 
     @property
     def scale(self):
@@ -101,24 +108,23 @@ def make_inputs(w: Workload, with_do: bool = True):
         ck = torch.zeros(len(lk) + 1, dtype=torch.int32)
         cq[1:] = torch.cumsum(torch.tensor(lq, dtype=torch.int64), 0).to(torch.int32)
         ck[1:] = torch.cumsum(torch.tensor(lk, dtype=torch.int64), 0).to(torch.int32)
-        qshape = (int(cq[-1]), w.hq, w.d)
-        kshape = (int(ck[-1]), w.hkv, w.d)
+        lead_q, lead_k = (int(cq[-1]),), (int(ck[-1]),)
     else:
         lq, lk = [w.sq] * w.batch, [w.skv] * w.batch
         cq = ck = None
-        qshape = (w.batch, w.sq, w.hq, w.d)
-        kshape = (w.batch, w.skv, w.hkv, w.d)
-    q = torch.randn(qshape, generator=gen, dtype=torch.float32).to(dt)
-    k = torch.randn(kshape, generator=gen, dtype=torch.float32).to(dt)
-    v = torch.randn(kshape, generator=gen, dtype=torch.float32).to(dt)
-    do = torch.randn(qshape, generator=gen, dtype=torch.float32).to(dt) if with_do else None
+        lead_q, lead_k = (w.batch, w.sq), (w.batch, w.skv)
+    q = torch.randn(lead_q + (w.hq, w.d), generator=gen, dtype=torch.float32).to(dt)
+    k = torch.randn(lead_k + (w.hkv, w.d), generator=gen, dtype=torch.float32).to(dt)
+    v = torch.randn(lead_k + (w.hkv, w.d_v), generator=gen, dtype=torch.float32).to(dt)
+    do = torch.randn(lead_q + (w.hq, w.d_v), generator=gen, dtype=torch.float32).to(dt) if with_do else None
     return dict(q=q, k=k, v=v, do=do, seqlens_q=lq, seqlens_kv=lk, cu_seqlens_q=cq, cu_seqlens_kv=ck,
                 max_seqlen_q=max(lq) if lq else 0, max_seqlen_kv=max(lk) if lk else 0)
 
 
 def small(name="small", *, batch=1, hq=2, hkv=2, sq=64, skv=64, d=64, dtype="bf16", mask="causal_tl", seed=0,
-          seqlens=None, seqlens_kv=None, window_left=-1):
+          seqlens=None, seqlens_kv=None, window_left=-1, dv=0):
     """A test-sized workload with the same recipe."""
     return Workload(name, batch=batch, hq=hq, hkv=hkv, sq=sq, skv=skv, d=d, dtype=dtype, mask=mask, seed=seed,
                     seqlens=tuple(seqlens) if seqlens is not None else None,
-                    seqlens_kv=tuple(seqlens_kv) if seqlens_kv is not None else None, window_left=window_left)
+                    seqlens_kv=tuple(seqlens_kv) if seqlens_kv is not None else None, window_left=window_left,
+                    dv=dv)

@@ -95,6 +95,15 @@ def allowed_pairs(lq, lk, mask, window_left=-1):
     return total
 
 
+def flop_per_pair(w):
+    """Algorithmic FLOPs per allowed (query, key) pair and q-head, with Q/K head dim Dqk and V/O head
+    dim Dv (both D for a symmetric head): forward QK^T + PV; backward S recompute, dV, dP, dQ, dK;
+    per kernel: the dK/dV pass S, dP, dV, dK and the dQ pass its dQ product (its second S/dP recompute
+    is executed but not credited)."""
+    dqk, dv = w.d, w.d_v
+    return {"fwd": 2.0 * (dqk + dv), "bwd": 6.0 * dqk + 4.0 * dv, "bwd_dkdv": 4.0 * (dqk + dv), "bwd_dq": 2.0 * dqk}
+
+
 def cpu_baseline(w, x, budget_s=12.0, max_units=6):
     """Time the float64 oracle (forward + backward) on whole (sequence, kv-head) units."""
     import numpy as np
@@ -114,7 +123,9 @@ def cpu_baseline(w, x, budget_s=12.0, max_units=6):
         sdpa_bwd(f64["q"], f64["k"], f64["v"], f64["do"], mask, w.scale, cu_q, cu_k, units=[unit],
                  window_left=w.window_left)
         t_total += time.perf_counter() - t0
-        flops += 14.0 * w.d * grp * allowed_pairs([x["seqlens_q"][b]], [x["seqlens_kv"][b]], w.mask, w.window_left)
+        fp = flop_per_pair(w)
+        flops += (fp["fwd"] + fp["bwd"]) * grp * allowed_pairs([x["seqlens_q"][b]], [x["seqlens_kv"][b]], w.mask,
+                                                              w.window_left)
         done.append(unit)
         if t_total >= budget_s:
             break
@@ -140,9 +151,9 @@ def run(w, steps, warmup, want_events=True):
     if w.packed:
         kw.update(cu_seqlens_q=x["cu_seqlens_q"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
                   max_seqlen_q=x["max_seqlen_q"], max_seqlen_kv=x["max_seqlen_kv"])
-    p = sd.make_problem(q, k, v, q, w.mask, w.scale, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_kv"),
+    o = torch.empty(q.shape[:-1] + v.shape[-1:], dtype=q.dtype, device=dev)  # O has V's head dim
+    p = sd.make_problem(q, k, v, o, w.mask, w.scale, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_kv"),
                         x["max_seqlen_q"], x["max_seqlen_kv"], w.window_left)
-    o = torch.empty_like(q)
     lse_shape = (q.shape[0], q.shape[1]) if w.packed else (q.shape[0], q.shape[2], q.shape[1])
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -185,14 +196,14 @@ def run(w, steps, warmup, want_events=True):
 def merge_measure(w, parts=2, steps=20, warmup=3):
     """attn_merge of `parts` forward results over w's query side (the ring step's combination).
 
-    HBM-bound: per (row, head) it reads parts x (2*D + 4) bytes and writes 2*D + 4. Returns the
+    HBM-bound: per (row, head) it reads parts x (2*Dv + 4) bytes and writes 2*Dv + 4. Returns the
     average launch time (HIP events on the launch stream) and the achieved GB/s against 8 TB/s.
     """
     import torch
     import scaled_dot_product_02_amd as sd
     dev = torch.device("cuda:0")
     g = torch.Generator().manual_seed(7)
-    shape = (w.batch, w.sq, w.hq, w.d)
+    shape = (w.batch, w.sq, w.hq, w.d_v)
     o_parts = [torch.randn(shape, generator=g).to(w.torch_dtype).to(dev) for _ in range(parts)]
     lse_parts = [(torch.randn(w.batch, w.hq, w.sq, generator=g) * 4).to(dev) for _ in range(parts)]
     out = torch.empty(shape, dtype=w.torch_dtype, device=dev)
@@ -207,7 +218,7 @@ def merge_measure(w, parts=2, steps=20, warmup=3):
         b.record()
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    nbytes = w.batch * w.sq * w.hq * (parts + 1) * (2 * w.d + 4)
+    nbytes = w.batch * w.sq * w.hq * (parts + 1) * (2 * w.d_v + 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"what": f"attn_merge of {parts} forward results, query side of {w.name}", "parts": parts,
             "us": round(ms * 1e3, 2), "bytes": nbytes, "GB/s": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -256,11 +267,12 @@ def main():
     log(f"workload {w.name}: {w.note}")
     r = run(w, args.steps, args.warmup)
     d, pairs = w.d, r["pairs"]
-    f_fwd, f_bwd = 4.0 * d * pairs, 10.0 * d * pairs
+    fp = flop_per_pair(w)
+    f_fwd, f_bwd = fp["fwd"] * pairs, fp["bwd"] * pairs
     value = (f_fwd + f_bwd) / (r["ms_step"] * 1e-3) / 1e12
     km = r["kern_ms"]
-    algo_flops = {"fwd": 4.0 * d * pairs, "bwd_dkdv": 8.0 * d * pairs, "bwd_dq": 2.0 * d * pairs}
-    pre_bytes = r["nrows"] * w.hq * (2 * d * 2 + 4 + 8)
+    algo_flops = {n: fp[n] * pairs for n in ("fwd", "bwd_dkdv", "bwd_dq")}
+    pre_bytes = r["nrows"] * w.hq * (2 * w.d_v * 2 + 4 + 8)
     dom = max(km, key=km.get)
     if dom == "bwd_pre":
         ach = pre_bytes / (km[dom] * 1e-3) / 1e9
@@ -279,7 +291,8 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch if not w.packed else len(r["x"]["seqlens_q"]),
                    "heads_q": w.hq, "heads_kv": w.hkv, "seq_q": w.sq or r["x"]["max_seqlen_q"],
-                   "seq_kv": w.skv or r["x"]["max_seqlen_kv"], "head_dim": d, "mask": w.mask,
+                   "seq_kv": w.skv or r["x"]["max_seqlen_kv"], "head_dim": d, "head_dim_v": w.d_v,
+                   "mask": w.mask,
                    "layout": "thd" if w.packed else "bshd", "window_left": w.window_left, "allowed_pairs": pairs},
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
@@ -292,7 +305,8 @@ def main():
     if not args.no_extra and w.name == "dense_d128":
         w2 = WORKLOADS["dense_d512"]
         r2 = run(w2, max(3, args.steps // 6), 2)
-        f2 = 14.0 * w2.d * r2["pairs"]
+        fp2 = flop_per_pair(w2)
+        f2 = (fp2["fwd"] + fp2["bwd"]) * r2["pairs"]
         km2 = r2["kern_ms"]
         out["extra"] = {"dense_d512": {"tflops": round(f2 / (r2["ms_step"] * 1e-3) / 1e12, 2),
                                        "ms_per_step": round(r2["ms_step"], 4),

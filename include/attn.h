@@ -5,7 +5,9 @@
  *   TransformerEngine pull request 3527, "cuDNN FROST attention backend for head_dim in (256, 512],
  *   with context parallelism" - sections Approach, Verification and Scope: fused attention
  *   S = scale * Q K^T, one of the masks no_mask / causal / causal_bottom_right, softmax, O = P V,
- *   and a backward producing dQ, dK, dV; symmetric head dims; GQA and MHA; bshd-style layouts.
+ *   and a backward producing dQ, dK, dV; GQA and MHA; bshd-style layouts; head dims that are
+ *   multiples of 8 up to 512, padded to a compiled width, and the asymmetric Q/K vs V/O pair the
+ *   forward engine there lists.
  *   TransformerEngine pull request 3705 (FROST forward provider for context-parallel attention) -
  *   section Execution and supported scope: compact packed (THD) batches described by zero-based
  *   cumulative sequence lengths with no holes, checked on the device on every execution; the
@@ -38,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -69,6 +71,14 @@ typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL_TL = 1, ATTN_MASK_CAUSAL_BR 
 
 /* One attention problem. All tensors have a contiguous head dimension (stride 1).
  *
+ * Head dims (pull request 3527, section Scope: the backward engine there serves any multiple of 8
+ * up to 512 by padding to its compiled width, and the forward engine lists the pair (192, 128)):
+ * Q, K, dQ, dK have head_dim = D_qk elements per row, V, O, dO, dV have D_v = head_dim_v (or
+ * head_dim when head_dim_v is 0); each is a multiple of 8 in [8, 512]. A call runs on the smallest
+ * compiled width of 64, 128, 256, 512 that holds both, computing narrower heads as if padded with
+ * zero columns: nothing is copied, no workspace is added and no byte past a row's D is read or
+ * written. Below, D stands for the tensor's own head dim.
+ *
  * Dense batches (cu_seqlens_q == cu_seqlens_kv == NULL): Q, O, dO, dQ are logically [B, Sq, Hq, D]
  * and K, V, dK, dV are [B, Skv, Hkv, D], with element strides (batch, sequence, head) given in
  * *_stride[0..2]; Sq = max_seqlen_q, Skv = max_seqlen_kv for every batch element. This covers
@@ -92,7 +102,7 @@ typedef struct attn_problem {
   int32_t batch;       /* dense batch size or number of packed sequences (>= 0)       */
   int32_t heads_q;     /* Hq >= 1                                                     */
   int32_t heads_kv;    /* Hkv >= 1, Hq % Hkv == 0                                     */
-  int32_t head_dim;    /* D in {64, 128, 256, 512}                                    */
+  int32_t head_dim;    /* D_qk: head dim of Q, K (multiple of 8 in [8, 512])         */
   int32_t max_seqlen_q;  /* dense: Sq; packed: an upper bound of every query length   */
   int32_t max_seqlen_kv; /* dense: Skv; packed: an upper bound of every key length    */
   const int32_t* cu_seqlens_q;  /* device int32[batch + 1] or NULL (dense)            */
@@ -104,7 +114,7 @@ typedef struct attn_problem {
   int64_t v_stride[3];
   int64_t o_stride[3];
   int32_t window_left; /* sliding window below the causal diagonal (see above); -1 = none (ABI 2) */
-  int32_t reserved;    /* must be 0                                                   */
+  int32_t head_dim_v;  /* D_v: head dim of V, O (multiple of 8 in [8, 512]); 0 = head_dim (ABI 3) */
 } attn_problem_t;
 
 /* Workspace. Its first 256 bytes are a header whose int32 at offset 0 is the device error word:
@@ -161,8 +171,9 @@ attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k,
  * into o (p->o_stride) and lse. Parts with LSE_k = -inf contribute nothing; rows where every part is
  * -inf get O = 0, LSE = -inf. The result equals one attn_fwd over the union of the key sets (up to the
  * rounding of the parts), and merging is associative, so any number of chunks can be merged in steps.
- * Only the query side of p is used: abi_version, dtype, batch, heads_q, head_dim, max_seqlen_q,
- * o_stride, and for packed batches cu_seqlens_q (marks the layout; not read) and total_q. o may be
+ * Only the query side of p is used: abi_version, dtype, batch, heads_q, head_dim and head_dim_v (O
+ * has head_dim_v elements per row, or head_dim when head_dim_v is 0), max_seqlen_q, o_stride, and
+ * for packed batches cu_seqlens_q (marks the layout; not read) and total_q. o may be
  * exactly one of the o_parts and lse exactly one of the lse_parts (in-place accumulation); any other
  * overlap of an output with an input or with the other output is ATTN_E_OVERLAP. No workspace. */
 #define ATTN_MERGE_MAX_PARTS 8

@@ -14,7 +14,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsdpa02.so"
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
@@ -47,7 +47,7 @@ class AttnProblem(ctypes.Structure):
         ("v_stride", ctypes.c_int64 * 3),
         ("o_stride", ctypes.c_int64 * 3),
         ("window_left", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
     ]
 
 
@@ -136,6 +136,7 @@ def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_
     p.heads_q = q.shape[-2]
     p.heads_kv = k.shape[-2]
     p.head_dim = d
+    p.head_dim_v = 0 if v.shape[-1] == d else v.shape[-1]  # V/O head dim when it differs from Q/K's
     if packed:
         p.batch = cu_seqlens_q.numel() - 1
         p.total_q = q.shape[0]
@@ -189,13 +190,14 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
     """Forward through the C-ABI. Returns (O, LSE).
 
     Dense q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]; packed q [Tq,Hq,D], k/v [Tkv,Hkv,D] with int32
-    cu_seqlens on the device. LSE is fp32 [B,Hq,Sq] (dense) or [Tq,Hq] (packed).
+    cu_seqlens on the device. V (and O) may have their own head dim D_v; O is then [..., Hq, D_v].
+    LSE is fp32 [B,Hq,Sq] (dense) or [Tq,Hq] (packed).
     """
     import torch
     _check_device(q, k, v, out, cu_seqlens_q, cu_seqlens_kv)
     packed = cu_seqlens_q is not None
     if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        out = torch.empty(q.shape[:-1] + v.shape[-1:], dtype=q.dtype, device=q.device)
     if lse is None:
         shape = (q.shape[0], q.shape[1]) if packed else (q.shape[0], q.shape[2], q.shape[1])
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)

@@ -66,6 +66,20 @@ bool overlaps(const Extent& a, const Extent& b) {
 
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
+// Head dims (pull request 3527, section Scope: any multiple of 8 up to 512, padded to a compiled
+// width; an asymmetric Q/K vs V/O pair). head_dim_v = 0 means the same as head_dim.
+int head_dim_v(const attn_problem_t* p) { return p->head_dim_v ? p->head_dim_v : p->head_dim; }
+
+attn_status_t check_head_dims(const attn_problem_t* p) {
+  if (p->head_dim <= 0) return fail(ATTN_E_INVALID, "head_dim %d <= 0", p->head_dim);
+  if (p->head_dim_v < 0) return fail(ATTN_E_INVALID, "head_dim_v %d < 0", p->head_dim_v);
+  if (p->head_dim % 8 || p->head_dim > 512)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not a multiple of 8 in [8, 512]", p->head_dim);
+  if (p->head_dim_v % 8 || p->head_dim_v > 512)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim_v %d is not 0 or a multiple of 8 in [8, 512]", p->head_dim_v);
+  return ATTN_OK;
+}
+
 attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (!p) return fail(ATTN_E_INVALID, "problem pointer is NULL");
   if (p->abi_version != ATTN_ABI_VERSION)
@@ -79,9 +93,7 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (p->heads_q < 1 || p->heads_kv < 1) return fail(ATTN_E_INVALID, "head counts must be >= 1");
   if (p->heads_q % p->heads_kv)
     return fail(ATTN_E_INVALID, "heads_q %d is not a multiple of heads_kv %d", p->heads_q, p->heads_kv);
-  if (p->head_dim <= 0) return fail(ATTN_E_INVALID, "head_dim %d <= 0", p->head_dim);
-  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256 && p->head_dim != 512)
-    return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not built (64, 128, 256, 512)", p->head_dim);
+  if (attn_status_t st = check_head_dims(p)) return st;
   if (!isfinite(p->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
   if (!(p->scale > 0.f)) return fail(ATTN_E_UNSUPPORTED, "scale %g is not positive", (double)p->scale);
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
@@ -89,7 +101,6 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (p->window_left >= 0 && p->mask == ATTN_MASK_NONE)
     return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
                 p->window_left);
-  if (p->reserved != 0) return fail(ATTN_E_INVALID, "reserved field is %d, must be 0", p->reserved);
   const bool packed = p->cu_seqlens_q != nullptr;
   if (packed != (p->cu_seqlens_kv != nullptr))
     return fail(ATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_kv must both be set (packed) or both be NULL");
@@ -122,9 +133,10 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   return ATTN_OK;
 }
 
-Extent ext_q(const attn_problem_t* p, const void* base, const int64_t* st, bool kv, const Info& in) {
+// d: the tensor's head dim (head_dim for Q, K, dQ, dK; head_dim_v for V, O, dO, dV)
+Extent ext_q(const attn_problem_t* p, const void* base, const int64_t* st, bool kv, const Info& in, int d) {
   const int64_t rows = in.packed ? (kv ? p->total_kv : p->total_q) : (kv ? p->max_seqlen_kv : p->max_seqlen_q);
-  return extent16(base, st, in.packed, p->batch, rows, kv ? p->heads_kv : p->heads_q, p->head_dim);
+  return extent16(base, st, in.packed, p->batch, rows, kv ? p->heads_kv : p->heads_q, d);
 }
 
 Extent ext_lse(const attn_problem_t* p, const float* lse, const Info& in) {
@@ -155,6 +167,8 @@ sdpa::AttnShape make_shape(const attn_problem_t* p, const Info& in, void* ws, in
   s.skv = p->max_seqlen_kv;
   s.mask = p->mask;
   s.wl = p->window_left;
+  s.dqk = p->head_dim;
+  s.dv = head_dim_v(p);
   s.n_qtiles = (p->max_seqlen_q + qtile - 1) / qtile;
   s.total_q = in.packed ? p->total_q : 0;
   s.total_kv = in.packed ? p->total_kv : 0;
@@ -230,8 +244,9 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
     Info in;
     attn_status_t st = check_problem(p, &in);
     if (st != ATTN_OK) return st;
-    const Extent eq = ext_q(p, q, p->q_stride, false, in), ek = ext_q(p, k, p->k_stride, true, in),
-                 ev = ext_q(p, v, p->v_stride, true, in), eo = ext_q(p, o, p->o_stride, false, in),
+    const int dqk = p->head_dim, dv = head_dim_v(p);
+    const Extent eq = ext_q(p, q, p->q_stride, false, in, dqk), ek = ext_q(p, k, p->k_stride, true, in, dqk),
+                 ev = ext_q(p, v, p->v_stride, true, in, dv), eo = ext_q(p, o, p->o_stride, false, in, dv),
                  el = ext_lse(p, lse, in);
     if ((st = check_ptr(q, eq, "q")) || (st = check_ptr(k, ek, "k")) || (st = check_ptr(v, ev, "v")) ||
         (st = check_ptr(o, eo, "o")))
@@ -257,7 +272,8 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
     if (p->batch == 0 || in.nq == 0) return ATTN_OK;  // no query row: nothing to write
 
     sdpa::FwdArgs a{};
-    a.s = make_shape(p, in, ws, sdpa::fwd_query_tile(p->head_dim));
+    const int inst = sdpa::instance_head_dim(dqk, dv);
+    a.s = make_shape(p, in, ws, sdpa::fwd_query_tile(inst));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -273,7 +289,7 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
       if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
     }
     if (a.s.n_qtiles == 0) return ATTN_OK;
-    const int e = sdpa::launch_fwd(p->dtype, p->head_dim, a, stream);
+    const int e = sdpa::launch_fwd(p->dtype, inst, a, stream);
     if (e) return fail(ATTN_E_HIP, "forward launch: %s", hipGetErrorString((hipError_t)e));
     return ATTN_OK;
   } catch (...) {
@@ -292,11 +308,12 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     Info in;
     attn_status_t st = check_problem(p, &in);
     if (st != ATTN_OK) return st;
-    const Extent eq = ext_q(p, q, p->q_stride, false, in), ek = ext_q(p, k, p->k_stride, true, in),
-                 ev = ext_q(p, v, p->v_stride, true, in), eo = ext_q(p, o, p->o_stride, false, in),
-                 edo = ext_q(p, d_o, p->o_stride, false, in), el = ext_lse(p, lse, in),
-                 edq = ext_q(p, dq, p->q_stride, false, in), edk = ext_q(p, dk, p->k_stride, true, in),
-                 edv = ext_q(p, dv, p->v_stride, true, in);
+    const int dqk = p->head_dim, dvw = head_dim_v(p);
+    const Extent eq = ext_q(p, q, p->q_stride, false, in, dqk), ek = ext_q(p, k, p->k_stride, true, in, dqk),
+                 ev = ext_q(p, v, p->v_stride, true, in, dvw), eo = ext_q(p, o, p->o_stride, false, in, dvw),
+                 edo = ext_q(p, d_o, p->o_stride, false, in, dvw), el = ext_lse(p, lse, in),
+                 edq = ext_q(p, dq, p->q_stride, false, in, dqk), edk = ext_q(p, dk, p->k_stride, true, in, dqk),
+                 edv = ext_q(p, dv, p->v_stride, true, in, dvw);
     if ((st = check_ptr(q, eq, "q")) || (st = check_ptr(k, ek, "k")) || (st = check_ptr(v, ev, "v")) ||
         (st = check_ptr(o, eo, "o")) || (st = check_ptr(d_o, edo, "d_o")) || (st = check_ptr(dq, edq, "dq")) ||
         (st = check_ptr(dk, edk, "dk")) || (st = check_ptr(dv, edv, "dv")))
@@ -323,7 +340,8 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     if (p->batch == 0 || (in.nq == 0 && in.nkv == 0)) return ATTN_OK;
 
     sdpa::BwdArgs a{};
-    a.s = make_shape(p, in, ws, sdpa::bwd_query_tile(p->head_dim));
+    const int inst = sdpa::instance_head_dim(dqk, dvw);
+    a.s = make_shape(p, in, ws, sdpa::bwd_query_tile(inst));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -341,13 +359,13 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     a.av = addr(p->v_stride, in.packed);
     a.ao = addr(p->o_stride, in.packed);
     a.alse = lse_addr(p, in.packed);
-    const int kt = sdpa::bwd_key_tile(p->head_dim);
+    const int kt = sdpa::bwd_key_tile(inst);
     a.n_kvtiles = (p->max_seqlen_kv + kt - 1) / kt;
     if (in.packed && (passes & sdpa::kPassPre)) {
       const int e = sdpa::launch_validate_cu(a.s, stream);
       if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
     }
-    const int e = sdpa::launch_bwd(p->dtype, p->head_dim, a, passes, stream);
+    const int e = sdpa::launch_bwd(p->dtype, inst, a, passes, stream);
     if (e) return fail(ATTN_E_HIP, "backward launch: %s", hipGetErrorString((hipError_t)e));
     return ATTN_OK;
   } catch (...) {
@@ -398,8 +416,8 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
       return fail(ATTN_E_UNSUPPORTED, "dtype %d is not bf16 (0) or fp16 (1)", p->dtype);
     if (p->batch < 0) return fail(ATTN_E_INVALID, "batch %d < 0", p->batch);
     if (p->heads_q < 1) return fail(ATTN_E_INVALID, "heads_q must be >= 1");
-    if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256 && p->head_dim != 512)
-      return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not built (64, 128, 256, 512)", p->head_dim);
+    if (attn_status_t hs = check_head_dims(p)) return hs;
+    const int dv = head_dim_v(p);  // the width of O
     if (p->max_seqlen_q < 0) return fail(ATTN_E_INVALID, "negative max_seqlen_q");
     if (n_parts < 1 || n_parts > ATTN_MERGE_MAX_PARTS)
       return fail(ATTN_E_INVALID, "n_parts %d is not in [1, %d]", n_parts, ATTN_MERGE_MAX_PARTS);
@@ -416,14 +434,14 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
         return fail(ATTN_E_ALIGN, "o_stride[%d] = %lld is not a multiple of 8 elements (16 bytes)", i,
                     (long long)p->o_stride[i]);
     }
-    const Extent eo = ext_q(p, o, p->o_stride, false, in), el = ext_lse(p, lse, in);
+    const Extent eo = ext_q(p, o, p->o_stride, false, in, dv), el = ext_lse(p, lse, in);
     attn_status_t st = check_ptr(o, eo, "o");
     if (st) return st;
     if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
     if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
     if (overlaps(eo, el)) return fail(ATTN_E_OVERLAP, "o overlaps lse");
     for (int k = 0; k < n_parts; ++k) {
-      const Extent ok = ext_q(p, o_parts[k], p->o_stride, false, in), lk = ext_lse(p, lse_parts[k], in);
+      const Extent ok = ext_q(p, o_parts[k], p->o_stride, false, in, dv), lk = ext_lse(p, lse_parts[k], in);
       if ((st = check_ptr(o_parts[k], ok, "o_parts[k]"))) return st;
       if (!lk.empty() && !lse_parts[k]) return fail(ATTN_E_INVALID, "lse_parts[%d] is NULL", k);
       if (!lk.empty() && !aligned(lse_parts[k], 4)) return fail(ATTN_E_ALIGN, "lse_parts[%d] is not 4-byte aligned", k);
@@ -447,10 +465,11 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
     a.hq = p->heads_q;
     a.sq = p->max_seqlen_q;
     a.packed = in.packed ? 1 : 0;
+    a.dv = dv;
     a.nrows = in.nq * p->heads_q;
     a.ao = addr(p->o_stride, in.packed);
     a.alse = lse_addr(p, in.packed);
-    const int e = sdpa::launch_merge(p->dtype, p->head_dim, a, stream);
+    const int e = sdpa::launch_merge(p->dtype, sdpa::instance_head_dim(dv, dv), a, stream);
     if (e) return fail(ATTN_E_HIP, "merge launch: %s", hipGetErrorString((hipError_t)e));
     return ATTN_OK;
   } catch (...) {

@@ -22,6 +22,7 @@ struct AttnShape {
   int32_t sq, skv;                // dense lengths, or the host-side maxima for packed batches
   int32_t mask;                   // attn_mask_t
   int32_t wl;                     // sliding window below the diagonal, -1 = none (causal masks only)
+  int32_t dqk, dv;                // head dims of Q/K and of V/O (multiples of 8, <= the kernel's D)
   int32_t n_qtiles;               // ceil(sq / query tile) of the launched kernel
   int64_t total_q, total_kv;      // packed token counts (for NaN fill on device errors)
   float scale;                    // softmax scale
@@ -67,11 +68,14 @@ struct MergeArgs {
   int32_t n_parts;
   int32_t hq, sq;     // sq: dense sequence length (unused for packed)
   int32_t packed;
+  int32_t dv;         // head dim of O (multiple of 8, <= the kernel's D)
   int64_t nrows;      // tokens * hq
   TensorAddr ao, alse;
 };
 
-// Launchers (attn_kernels.hip). Return hipError_t as int.
+// Launchers (attn_kernels.hip). Return hipError_t as int. head_dim is the compiled width a call runs
+// on (instance_head_dim); heads narrower than it (s.dqk, s.dv) run on the padded instances.
+int instance_head_dim(int dqk, int dv);  // smallest of 64, 128, 256, 512 holding both, 0 if none
 int launch_validate_cu(const AttnShape& s, void* stream);
 int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream);
 // Backward passes selected by bit: 1 = preprocess, 2 = dK/dV pass, 4 = dQ pass.

@@ -99,18 +99,33 @@ struct QueryWalk {
 // clamps the lane's row and forms its offsets (a few VALU operations per copy) where registers are
 // short. A tile that runs past the sequence end clamps each row to its last valid row (the repeated
 // rows are masked by the kernels).
-template <int D, int ROWS, int NDMA, bool KEEP = true>
+// PAD: X and Y rows hold only xd / yd (<= D, multiples of 8) elements; a lane whose chunk lies
+// beyond that copies nothing (its LDS slot keeps the zeros the kernel wrote there at start), so no
+// byte past a row's real width is read. The chunk of slot i depends on its row (swizzle), hence
+// one bit per slot.
+template <int D, int ROWS, int NDMA, bool KEEP = true, bool PAD = false>
 struct TileDma {
   static constexpr int CH = D / 8;
   static_assert((ROWS * CH) % (NDMA * 64) == 0, "a tile is a whole number of wave slots");
+  static_assert(NDMA <= 32, "one mask bit per slot");
   unsigned xo[KEEP ? NDMA : 1], yo[KEEP ? NDMA : 1];
   int slot0, lane;
   unsigned xrs, yrs;
-  __device__ __forceinline__ TileDma(int wslot, int lane_, int64_t xrow, int64_t yrow)
-      : slot0(wslot * NDMA * 64), lane(lane_), xrs((unsigned)xrow), yrs((unsigned)yrow) {
+  unsigned xm, ym;  // PAD: bit i set when slot i's chunk lies inside X's / Y's real width
+  __device__ __forceinline__ TileDma(int wslot, int lane_, int64_t xrow, int64_t yrow, int xd = D, int yd = D)
+      : slot0(wslot * NDMA * 64), lane(lane_), xrs((unsigned)xrow), yrs((unsigned)yrow), xm(0), ym(0) {
     if constexpr (KEEP) {
 #pragma unroll
       for (int i = 0; i < NDMA; ++i) offsets(lane, i, ROWS, xo[i], yo[i]);
+    }
+    if constexpr (PAD) {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) {
+        const int L = slot0 + i * 64 + lane;
+        const int c = (L % CH) ^ sw_key<D>(L / CH);
+        xm |= (8 * c < xd ? 1u : 0u) << i;
+        ym |= (8 * c < yd ? 1u : 0u) << i;
+      }
     }
   }
   // byte offsets of slot i's chunk for this lane, its row clamped to last
@@ -134,8 +149,8 @@ struct TileDma {
       } else {
         offsets(lane, i, last, xb, yb);
       }
-      dma16((const char*)xt + xb, xs + (slot0 + i * 64) * 8);
-      dma16((const char*)yt + yb, ys + (slot0 + i * 64) * 8);
+      if (!PAD || ((xm >> i) & 1u)) dma16((const char*)xt + xb, xs + (slot0 + i * 64) * 8);
+      if (!PAD || ((ym >> i) & 1u)) dma16((const char*)yt + yb, ys + (slot0 + i * 64) * 8);
     }
   }
 };
@@ -155,10 +170,10 @@ __device__ __forceinline__ int64_t flat_grid_threads() {
   return (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
 }
 
-// Fill a packed [tokens, heads, D] tensor with NaN (grid-stride over all workgroups).
-template <int D, typename T>
-__device__ void fill_nan_rows(void* base, const TensorAddr& a, int64_t tokens, int heads) {
-  constexpr int CH = D / 8;
+// Fill a packed [tokens, heads, d] tensor with NaN (grid-stride over all workgroups).
+template <typename T>
+__device__ void fill_nan_rows(void* base, const TensorAddr& a, int64_t tokens, int heads, int d) {
+  const int CH = d / 8;
   v8s nanv;
   for (int i = 0; i < 8; ++i) nanv[i] = (short)nan_bits<T>();
   const int64_t n = tokens * heads * CH;
@@ -167,6 +182,22 @@ __device__ void fill_nan_rows(void* base, const TensorAddr& a, int64_t tokens, i
     const int rem = (int)(i % (heads * CH));
     *reinterpret_cast<v8s*>((us*)base + t * a.row + (int64_t)(rem / CH) * a.head + (rem % CH) * 8) = nanv;
   }
+}
+
+// Heads narrower than the kernel's D (PAD instances) are computed as if padded with zero columns:
+// zero columns add nothing to Q K^T or dO V^T, and the padded columns of O, dQ, dK, dV are never
+// stored. A chunk of 8 elements starting at column col is inside a head of width d (a multiple of 8)
+// or wholly outside it.
+template <bool PAD>
+__device__ __forceinline__ v8s ld_chunk(const us* p, int col, int d) {
+  if (PAD && col >= d) return v8s{};
+  return *reinterpret_cast<const v8s*>(p);
+}
+// Zero N 16-bit LDS elements with the whole workgroup (the caller then synchronises).
+template <int N>
+__device__ __forceinline__ void zero_lds(us* p) {
+  static_assert(N % 8 == 0, "whole 16-byte chunks");
+  for (int i = threadIdx.x; i < N / 8; i += blockDim.x) reinterpret_cast<v8s*>(p)[i] = v8s{};
 }
 
 // ------------------------------------------------------------------------------------------
@@ -211,7 +242,7 @@ __global__ void __launch_bounds__(256) validate_cu_kernel(AttnShape s) {
 // ------------------------------------------------------------------------------------------
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int BN, int MINW, typename T>
+template <int D, int BN, int MINW, typename T, bool PAD>
 __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
   constexpr int CH = D / 8;
@@ -222,7 +253,7 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
-    fill_nan_rows<D, T>(a.o, a.ao, s.total_q, s.hq);
+    fill_nan_rows<T>(a.o, a.ao, s.total_q, s.hq, s.dv);
     for (int64_t i = flat_block() * blockDim.x + threadIdx.x; i < s.total_q * s.hq; i += flat_grid_threads())
       a.lse[(i / s.hq) * a.alse.row + (i % s.hq) * a.alse.head] = __builtin_nanf("");
     return;
@@ -253,7 +284,7 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   {
     const us* p = qg + (int64_t)min(qi, sq.sq - 1) * a.aq.row + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const v8s*>(p + 16 * kk);
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = ld_chunk<PAD>(p + 16 * kk, 16 * kk + 8 * hh, s.dqk);
   }
   v16f oacc[D / 32];
 #pragma unroll
@@ -261,7 +292,7 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   float m_ref = -__builtin_inff();  // scaled (log2-domain) reference of this row
   float l_run = 0.f;                // this lane's half of the row sum, relative to m_ref
 
-  const TileDma<D, BN, NDMA> dma(w, lane, a.ak.row, a.av.row);
+  const TileDma<D, BN, NDMA, true, PAD> dma(w, lane, a.ak.row, a.av.row, s.dqk, s.dv);
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * TILE;
     us* vs = ks + TILE;
@@ -279,6 +310,10 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   int vkey[2];
 #pragma unroll
   for (int cp = 0; cp < 2; ++cp) vkey[cp] = (sw_key<D>(8 * cp + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3;
+  if constexpr (PAD) {
+    zero_lds<2 * 2 * TILE>(smem);
+    __syncthreads();
+  }
   if (j0 < n_tiles) issue(j0, j0 & 1);
   for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
@@ -385,7 +420,8 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
         v[1] = Elem<T>::cvt(oacc[dt][4 * q4 + 1] * inv);
         v[2] = Elem<T>::cvt(oacc[dt][4 * q4 + 2] * inv);
         v[3] = Elem<T>::cvt(oacc[dt][4 * q4 + 3] * inv);
-        *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
+        if (!PAD || 32 * dt + 8 * q4 + 4 * hh < s.dv)
+          *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
       }
     if (hh == 0) {
       float* lp = a.lse + seq_off(a.alse, packed, b, sq.tq0) + (int64_t)h * a.alse.head + (int64_t)qi * a.alse.row;
@@ -404,7 +440,7 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
 // bits), then both run the identical softmax and each accumulates O^T for its half of D. Every
 // wave executes every barrier; a wave pair with no allowed key in a tile skips only its MFMAs.
 // ------------------------------------------------------------------------------------------
-template <int D, typename T>
+template <int D, typename T, bool PAD>
 __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   constexpr int BM = 128, BN = 32, NW = 8, DH = D / 2;
   constexpr int CH = D / 8;
@@ -416,7 +452,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
-    fill_nan_rows<D, T>(a.o, a.ao, s.total_q, s.hq);
+    fill_nan_rows<T>(a.o, a.ao, s.total_q, s.hq, s.dv);
     for (int64_t i = flat_block() * blockDim.x + threadIdx.x; i < s.total_q * s.hq; i += flat_grid_threads())
       a.lse[(i / s.hq) * a.alse.row + (i % s.hq) * a.alse.head] = __builtin_nanf("");
     return;
@@ -448,7 +484,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   {
     const us* p = qg + (int64_t)min(qi, sq.sq - 1) * a.aq.row + hf * DH + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = *reinterpret_cast<const v8s*>(p + 16 * kk);
+    for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = ld_chunk<PAD>(p + 16 * kk, hf * DH + 16 * kk + 8 * hh, s.dqk);
   }
   v16f oacc[DH / 32];
 #pragma unroll
@@ -456,7 +492,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   float m_ref = -__builtin_inff();
   float l_run = 0.f;
 
-  const TileDma<D, BN, NDMA, (D < 512)> dma(w, lane, a.ak.row, a.av.row);  // registers are short at D = 512
+  const TileDma<D, BN, NDMA, (D < 512), PAD> dma(w, lane, a.ak.row, a.av.row, s.dqk, s.dv);  // registers are short at D = 512
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * TILE;
     us* vs = ks + TILE;
@@ -474,6 +510,10 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   int vkey[2];
 #pragma unroll
   for (int cp = 0; cp < 2; ++cp) vkey[cp] = (sw_key<D>(8 * cp + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3;
+  if constexpr (PAD) {
+    zero_lds<2 * 2 * TILE>(smem);
+    __syncthreads();
+  }
   if (j0 < n_tiles) issue(j0, j0 & 1);
   for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
@@ -563,7 +603,8 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
         v[1] = Elem<T>::cvt(oacc[dt][4 * q4 + 1] * inv);
         v[2] = Elem<T>::cvt(oacc[dt][4 * q4 + 2] * inv);
         v[3] = Elem<T>::cvt(oacc[dt][4 * q4 + 3] * inv);
-        *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
+        if (!PAD || hf * DH + 32 * dt + 8 * q4 + 4 * hh < s.dv)
+          *reinterpret_cast<typename Elem<T>::op4*>(op + 32 * dt + 8 * q4 + 4 * hh) = v;
       }
     if (hh == 0 && hf == 0) {
       float* lp = a.lse + seq_off(a.alse, packed, b, sq.tq0) + (int64_t)h * a.alse.head + (int64_t)qi * a.alse.row;
@@ -601,10 +642,12 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
       oofs = bb * a.ao.batch + si * a.ao.row + (int64_t)h * a.ao.head;
       lofs = bb * a.alse.batch + si * a.alse.row + (int64_t)h * a.alse.head;
     }
-    const v8s o8 = *reinterpret_cast<const v8s*>((const us*)a.o + oofs + 8 * c);
-    const v8s d8 = *reinterpret_cast<const v8s*>((const us*)a.d_o + oofs + 8 * c);
+    if (8 * c < s.dv) {  // lanes past a narrower head's width contribute 0
+      const v8s o8 = *reinterpret_cast<const v8s*>((const us*)a.o + oofs + 8 * c);
+      const v8s d8 = *reinterpret_cast<const v8s*>((const us*)a.d_o + oofs + 8 * c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc += to_f32<T>(o8[i]) * to_f32<T>(d8[i]);
+      for (int i = 0; i < 8; ++i) acc += to_f32<T>(o8[i]) * to_f32<T>(d8[i]);
+    }
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -625,7 +668,7 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
 //   dV += P^T dO, dK += dS^T Q  (A = the P / dS accumulators as they are, B = dO / Q by transpose
 //   reads). dK is scaled once at the end; keys no query sees get exact zeros.
 // ------------------------------------------------------------------------------------------
-template <int D, int KB, int MINW, typename T>
+template <int D, int KB, int MINW, typename T, bool PAD>
 __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NW = 4, KW = 16 * KB, BKV = NW * KW, BQ = D <= 128 ? 64 : 32, QH = BQ / 32, CH = D / 8;
   constexpr int QTILE = BQ * D;
@@ -636,8 +679,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
-    fill_nan_rows<D, T>(a.dk, a.ak, s.total_kv, s.hkv);
-    fill_nan_rows<D, T>(a.dv, a.av, s.total_kv, s.hkv);
+    fill_nan_rows<T>(a.dk, a.ak, s.total_kv, s.hkv, s.dqk);
+    fill_nan_rows<T>(a.dv, a.av, s.total_kv, s.hkv, s.dv);
     return;
   }
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -665,8 +708,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     const int64_t r = min(kw0 + 16 * kb + l16, sq.skv - 1);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      kf[kb][kk] = *reinterpret_cast<const v8s*>(kg + r * a.ak.row + 32 * kk + 8 * G);
-      vf[kb][kk] = *reinterpret_cast<const v8s*>(vg + r * a.av.row + 32 * kk + 8 * G);
+      kf[kb][kk] = ld_chunk<PAD>(kg + r * a.ak.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dqk);
+      vf[kb][kk] = ld_chunk<PAD>(vg + r * a.av.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dv);
     }
   }
   v4f dk[KB][D / 16], dv[KB][D / 16];
@@ -678,7 +721,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       dv[kb][dt] = v4f{};
     }
 
-  const TileDma<D, BQ, NDMA, (D != 128)> dma(w, lane, a.aq.row, a.ao.row);  // registers are short at D = 128
+  const TileDma<D, BQ, NDMA, (D != 128), PAD> dma(w, lane, a.aq.row, a.ao.row, s.dqk, s.dv);  // registers are short at D = 128
   QueryWalk<BQ> ld(a, packed, b, sq, g * s.group, qt0, nq);
   const int qt_end = qt0 + nq;
   auto issue = [&](int stage) {
@@ -703,6 +746,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   static_assert((STAGE & (D - 1)) == 0 && (QTILE & (D - 1)) == 0, "stage offsets must leave the chunk bits alone");
   int qt_c = qt0;  // query tile of the iteration
+  if constexpr (PAD) {
+    zero_lds<2 * STAGE>(smem);
+    __syncthreads();
+  }
   if (n_it > 0) issue(0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
@@ -805,8 +852,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       if (key < sq.skv) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          dkp[(int64_t)key * a.ak.row + 16 * dt + l16] = Elem<T>::cvt(dk[kb][dt][i] * s.scale);
-          dvp[(int64_t)key * a.av.row + 16 * dt + l16] = Elem<T>::cvt(dv[kb][dt][i]);
+          if (!PAD || 16 * dt + l16 < s.dqk)
+            dkp[(int64_t)key * a.ak.row + 16 * dt + l16] = Elem<T>::cvt(dk[kb][dt][i] * s.scale);
+          if (!PAD || 16 * dt + l16 < s.dv) dvp[(int64_t)key * a.av.row + 16 * dt + l16] = Elem<T>::cvt(dv[kb][dt][i]);
         }
       }
     }
@@ -819,7 +867,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
 //   P = exp2(S*c - lse2), dS = P (dP - D)            (lse2, D are per-lane scalars)
 //   dQ += dS K                  (A = the dS accumulators, B = K by transpose reads)
 // ------------------------------------------------------------------------------------------
-template <int D, int QB, int MINW, typename T>
+template <int D, int QB, int MINW, typename T, bool PAD>
 __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   // key tiles of BK = 64 (D <= 128) or 32 keys, processed as 32-key halves: a larger tile halves the
   // barriers, waits and copy issues per key at the same register use
@@ -831,7 +879,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
-    fill_nan_rows<D, T>(a.dq, a.aq, s.total_q, s.hq);
+    fill_nan_rows<T>(a.dq, a.aq, s.total_q, s.hq, s.dqk);
     return;
   }
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -862,8 +910,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     const int64_t r = min(qw0 + 16 * qb + l16, sq.sq - 1);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      qf[qb][kk] = *reinterpret_cast<const v8s*>(qg + r * a.aq.row + 32 * kk + 8 * G);
-      df[qb][kk] = *reinterpret_cast<const v8s*>(dg + r * a.ao.row + 32 * kk + 8 * G);
+      qf[qb][kk] = ld_chunk<PAD>(qg + r * a.aq.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dqk);
+      df[qb][kk] = ld_chunk<PAD>(dg + r * a.ao.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dv);
     }
     l2[qb] = a.lse2[(int64_t)h * a.nrows + rowbase + r];
     dr[qb] = a.rowsum[(int64_t)h * a.nrows + rowbase + r];
@@ -874,7 +922,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) dq[qb][dt] = v4f{};
 
-  const TileDma<D, BK, NDMA> dma(w, lane, a.ak.row, a.av.row);
+  const TileDma<D, BK, NDMA, true, PAD> dma(w, lane, a.ak.row, a.av.row, s.dqk, s.dv);
   auto issue = [&](int tile, int stage) {
     us* ks = smem + stage * 2 * KTILE;
     us* vs = ks + KTILE;
@@ -886,6 +934,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
+  if constexpr (PAD) {
+    zero_lds<2 * 2 * KTILE>(smem);
+    __syncthreads();
+  }
   if (j0 < n_tiles) issue(j0, j0 & 1);
   for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
@@ -970,7 +1022,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
       if (q < sq.sq) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-          dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[qb][dt][i] * s.scale);
+          if (!PAD || 16 * dt + l16 < s.dqk)
+            dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[qb][dt][i] * s.scale);
       }
     }
 }
@@ -987,7 +1040,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 // computes dP, they swap (fp32), both form the same dS, and each accumulates half of dQ's columns.
 // Every wave executes every barrier; a pair whose keys / rows see nothing in a tile skips its MFMAs.
 // ------------------------------------------------------------------------------------------
-template <int D, typename T>
+template <int D, typename T, bool PAD>
 __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   constexpr int NW = 8, KW = 16, BKV = 4 * KW, BQ = 32, CH = D / 8;
   constexpr int QTILE = BQ * D;
@@ -999,8 +1052,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
-    fill_nan_rows<D, T>(a.dk, a.ak, s.total_kv, s.hkv);
-    fill_nan_rows<D, T>(a.dv, a.av, s.total_kv, s.hkv);
+    fill_nan_rows<T>(a.dk, a.ak, s.total_kv, s.hkv, s.dqk);
+    fill_nan_rows<T>(a.dv, a.av, s.total_kv, s.hkv, s.dv);
     return;
   }
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -1028,14 +1081,15 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   v8s kvf[D / 32];
   {
     const int64_t r = min(kw0 + l16, sq.skv - 1);
+    const int kvd = role == 0 ? s.dqk : s.dv;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) kvf[kk] = *reinterpret_cast<const v8s*>(kvg + r * kvrow + 32 * kk + 8 * G);
+    for (int kk = 0; kk < D / 32; ++kk) kvf[kk] = ld_chunk<PAD>(kvg + r * kvrow + 32 * kk + 8 * G, 32 * kk + 8 * G, kvd);
   }
   v4f acc[D / 16];  // dV (role 0) or dK (role 1): key kw0 + 4G + i, d = 16dt + l16
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = v4f{};
 
-  const TileDma<D, BQ, NDMA> dma(w, lane, a.aq.row, a.ao.row);
+  const TileDma<D, BQ, NDMA, true, PAD> dma(w, lane, a.aq.row, a.ao.row, s.dqk, s.dv);
   QueryWalk<BQ> ld(a, packed, b, sq, g * s.group, qt0, nq);
   const int qt_end = qt0 + nq;
   auto issue = [&](int stage) {
@@ -1058,6 +1112,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   float* pbuf = xch + pr * 2 * 64 * 4;
 
   int qt_c = qt0;  // query tile of the iteration
+  if constexpr (PAD) {
+    zero_lds<2 * STAGE>(smem);
+    __syncthreads();
+  }
   if (n_it > 0) issue(0);
   for (int it = 0; it < n_it; ++it) {
     wait_vmem();
@@ -1130,17 +1188,19 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
                       : (T*)a.dk + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
   const int64_t orow = role == 0 ? a.av.row : a.ak.row;
   const float oscale = role == 0 ? 1.f : s.scale;
+  const int od = role == 0 ? s.dv : s.dqk;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int key = kw0 + 4 * G + i;
     if (key < sq.skv) {
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) outp[(int64_t)key * orow + 16 * dt + l16] = Elem<T>::cvt(acc[dt][i] * oscale);
+      for (int dt = 0; dt < D / 16; ++dt)
+        if (!PAD || 16 * dt + l16 < od) outp[(int64_t)key * orow + 16 * dt + l16] = Elem<T>::cvt(acc[dt][i] * oscale);
     }
   }
 }
 
-template <int D, typename T>
+template <int D, typename T, bool PAD>
 __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   constexpr int NW = 8, QW = 16, BMQ = 4 * QW, BK = 32, CH = D / 8, DH = D / 2;
   constexpr int KTILE = BK * D;
@@ -1151,7 +1211,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
-    fill_nan_rows<D, T>(a.dq, a.aq, s.total_q, s.hq);
+    fill_nan_rows<T>(a.dq, a.aq, s.total_q, s.hq, s.dqk);
     return;
   }
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -1181,8 +1241,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   float l2, dr;
   {
     const int64_t r = min(qw0 + l16, sq.sq - 1);
+    const int qdd = role == 0 ? s.dqk : s.dv;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) qdf[kk] = *reinterpret_cast<const v8s*>(qdg + r * qdrow + 32 * kk + 8 * G);
+    for (int kk = 0; kk < D / 32; ++kk) qdf[kk] = ld_chunk<PAD>(qdg + r * qdrow + 32 * kk + 8 * G, 32 * kk + 8 * G, qdd);
     l2 = a.lse2[(int64_t)h * a.nrows + rowbase + r];
     dr = a.rowsum[(int64_t)h * a.nrows + rowbase + r];
   }
@@ -1190,7 +1251,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DH / 16; ++dt) dq[dt] = v4f{};
 
-  const TileDma<D, BK, NDMA> dma(w, lane, a.ak.row, a.av.row);
+  const TileDma<D, BK, NDMA, true, PAD> dma(w, lane, a.ak.row, a.av.row, s.dqk, s.dv);
   // issue() is called for tiles j0, j0 + 1, ... in order: running tile pointers
   const int64_t kstep = (int64_t)BK * a.ak.row, vstep = (int64_t)BK * a.av.row;
   const us* k_ld = kg + j0 * kstep;
@@ -1209,6 +1270,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   float* mine = xch + w * 2 * 64 * 4;
   const float* other = xch + (w ^ 4) * 2 * 64 * 4;
 
+  if constexpr (PAD) {
+    zero_lds<2 * 2 * KTILE>(smem);
+    __syncthreads();
+  }
   if (j0 < n_tiles) issue(j0, j0 & 1);
   for (int j = j0; j < n_tiles; ++j) {
     wait_vmem();
@@ -1278,7 +1343,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     const int q = qw0 + 4 * G + i;
     if (q < sq.sq) {
 #pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[dt][i] * s.scale);
+      for (int dt = 0; dt < DH / 16; ++dt)
+        if (!PAD || role * DH + 16 * dt + l16 < s.dqk)
+          dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[dt][i] * s.scale);
     }
   }
 }
@@ -1321,6 +1388,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
     l[k] = k < a.n_parts ? a.lse_parts[k][lofs] : -__builtin_inff();
     m = fmaxf(m, l[k]);
   }
+  const bool col_live = 8 * c < a.dv;  // lanes past a narrower head's width read and write nothing
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -__builtin_inff()) {
@@ -1329,9 +1397,11 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
       if (k < a.n_parts) {
         const float wk = fast_exp2((l[k] - m) * kLog2e);  // 0 for an empty part
         tot += wk;
-        const v8s x = *reinterpret_cast<const v8s*>((const us*)a.o_parts[k] + oofs + 8 * c);
+        if (col_live) {
+          const v8s x = *reinterpret_cast<const v8s*>((const us*)a.o_parts[k] + oofs + 8 * c);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk, to_f32<T>(x[i]), acc[i]);
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wk, to_f32<T>(x[i]), acc[i]);
+        }
       }
     }
   }
@@ -1339,7 +1409,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(MergeArgs a) {
   typename Elem<T>::op8 r;
 #pragma unroll
   for (int i = 0; i < 8; ++i) r[i] = Elem<T>::cvt(acc[i] * inv);
-  *reinterpret_cast<typename Elem<T>::op8*>((T*)a.o + oofs + 8 * c) = r;
+  if (col_live) *reinterpret_cast<typename Elem<T>::op8*>((T*)a.o + oofs + 8 * c) = r;
   if (c == 0) a.lse[lofs] = tot > 0.f ? m + __builtin_log2f(tot) * kLn2 : -__builtin_inff();
 }
 
@@ -1347,6 +1417,11 @@ template <int D> constexpr int fwd_bn() { return D <= 128 ? 64 : 32; }
 template <int D> constexpr int dkdv_kb() { return D <= 128 ? 2 : 1; }
 template <int D> constexpr int dq_qb() { return D <= 128 ? 2 : 1; }
 template <int D> constexpr int bwd_minw() { return D <= 256 ? 2 : 1; }
+
+int instance_head_dim(int dqk, int dv) {
+  const int m = dqk > dv ? dqk : dv;
+  return m <= 64 ? 64 : m <= 128 ? 128 : m <= 256 ? 256 : m <= 512 ? 512 : 0;
+}
 
 int fwd_query_tile(int) { return kFwdBM; }
 int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }  // 64 for the D = 512 pair kernel too
@@ -1359,18 +1434,18 @@ int launch_validate_cu(const AttnShape& s, void* stream) {
 
 template <int D> constexpr int fwd_minw() { return D <= 256 ? 2 : 1; }
 
-template <int D, typename T>
+template <int D, typename T, bool PAD>
 static int fwd_t(const FwdArgs& a, hipStream_t st) {
   const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
   if constexpr (D <= 128) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd_split_kernel<D, T>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_split_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
   }
   return (int)hipGetLastError();
 }
 
-template <int D, typename T>
+template <int D, typename T, bool PAD>
 static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
   // Launches with an empty grid are skipped (e.g. no query rows: only dK = dV = 0 remain to write).
   constexpr int RPB = 256 / (D / 8);
@@ -1383,32 +1458,41 @@ static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
   if ((passes & kPassDkdv) && a.n_kvtiles > 0) {
     const dim3 grid(a.s.batch * a.s.hkv * a.n_kvtiles);
     if constexpr (D <= 256) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), bwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), bwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, T>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   if ((passes & kPassDq) && a.s.n_qtiles > 0) {
     const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
     if constexpr (D <= 256) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dq_pair_kernel<D, T>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((attn_bwd_dq_pair_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
   return (int)e;
 }
 
+// PAD instances serve heads narrower than D (either head dim below it); full-width heads keep the
+// unpadded code.
+template <int D>
+static int fwd_d(bool bf, const FwdArgs& a, hipStream_t st) {
+  const bool pad = a.s.dqk != D || a.s.dv != D;
+  if (bf) return pad ? fwd_t<D, __bf16, true>(a, st) : fwd_t<D, __bf16, false>(a, st);
+  return pad ? fwd_t<D, _Float16, true>(a, st) : fwd_t<D, _Float16, false>(a, st);
+}
+
 int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool bf = dtype == 0;
   switch (head_dim) {
-    case 64: return bf ? fwd_t<64, __bf16>(a, st) : fwd_t<64, _Float16>(a, st);
-    case 128: return bf ? fwd_t<128, __bf16>(a, st) : fwd_t<128, _Float16>(a, st);
-    case 256: return bf ? fwd_t<256, __bf16>(a, st) : fwd_t<256, _Float16>(a, st);
-    case 512: return bf ? fwd_t<512, __bf16>(a, st) : fwd_t<512, _Float16>(a, st);
+    case 64: return fwd_d<64>(bf, a, st);
+    case 128: return fwd_d<128>(bf, a, st);
+    case 256: return fwd_d<256>(bf, a, st);
+    case 512: return fwd_d<512>(bf, a, st);
   }
   return (int)hipErrorInvalidValue;
 }
@@ -1433,14 +1517,21 @@ int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream) {
   return (int)hipErrorInvalidValue;
 }
 
+template <int D>
+static int bwd_d(bool bf, const BwdArgs& a, int passes, hipStream_t st) {
+  const bool pad = a.s.dqk != D || a.s.dv != D;
+  if (bf) return pad ? bwd_t<D, __bf16, true>(a, passes, st) : bwd_t<D, __bf16, false>(a, passes, st);
+  return pad ? bwd_t<D, _Float16, true>(a, passes, st) : bwd_t<D, _Float16, false>(a, passes, st);
+}
+
 int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const bool bf = dtype == 0;
   switch (head_dim) {
-    case 64: return bf ? bwd_t<64, __bf16>(a, passes, st) : bwd_t<64, _Float16>(a, passes, st);
-    case 128: return bf ? bwd_t<128, __bf16>(a, passes, st) : bwd_t<128, _Float16>(a, passes, st);
-    case 256: return bf ? bwd_t<256, __bf16>(a, passes, st) : bwd_t<256, _Float16>(a, passes, st);
-    case 512: return bf ? bwd_t<512, __bf16>(a, passes, st) : bwd_t<512, _Float16>(a, passes, st);
+    case 64: return bwd_d<64>(bf, a, passes, st);
+    case 128: return bwd_d<128>(bf, a, passes, st);
+    case 256: return bwd_d<256>(bf, a, passes, st);
+    case 512: return bwd_d<512>(bf, a, passes, st);
   }
   return (int)hipErrorInvalidValue;
 }

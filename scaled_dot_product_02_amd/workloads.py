@@ -85,6 +85,10 @@ WORKLOADS = {
     "window_d256": Workload("window_d256", batch=1, hq=16, hkv=8, sq=8192, skv=8192, d=256, dtype="bf16",
                             mask="causal_tl", window_left=1023, seed=5,
                             note="B1 Hq16/Hkv8 S8192 D256 bf16 causal with a 1024-key sliding window"),
+    # the asymmetric head pair (Q/K 192, V/O 128) that pull request 3527 says the forward engine lists,
+    # at the dense D=128 shape; it runs on the D=256 kernels with padded columns
+    "asym_d192": Workload("asym_d192", batch=2, hq=16, hkv=16, sq=8192, skv=8192, d=192, dv=128, dtype="bf16",
+                          mask="causal_tl", seed=6, note="B2 H16/16 S8192 Dqk192/Dv128 bf16 causal top-left"),
 }
 
 

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.attn_abi_version() == 2
+    assert L.attn_abi_version() == 3
     for code, name in B.STATUS.items():
         assert L.attn_status_str(code).decode() == name
     assert L.attn_status_str(42).decode() == "ATTN_E_UNKNOWN"
@@ -49,7 +49,7 @@ def test_version_and_status_strings(L):
 
 def dense_problem(b=2, sq=256, skv=256, hq=4, hkv=2, d=128, dtype=0, mask=1):
     p = B.AttnProblem()
-    p.abi_version = 2
+    p.abi_version = 3
     p.window_left = -1  # no sliding window (ctypes zero-fills, and 0 is a window)
     p.dtype, p.mask, p.scale = dtype, mask, d ** -0.5
     p.batch, p.heads_q, p.heads_kv, p.head_dim = b, hq, hkv, d
@@ -94,14 +94,18 @@ def test_null_problem(L):
 
 
 @pytest.mark.parametrize("field,value,want,frag", [
-    ("abi_version", 1, UNSUPPORTED, "abi_version"),
-    ("abi_version", 3, UNSUPPORTED, "abi_version"),
+    ("abi_version", 2, UNSUPPORTED, "abi_version"),
+    ("abi_version", 4, UNSUPPORTED, "abi_version"),
     ("window_left", -2, INVALID, "window_left"),
-    ("reserved", 1, INVALID, "reserved"),
+    ("head_dim_v", -8, INVALID, "head_dim_v"),
+    ("head_dim_v", 100, UNSUPPORTED, "head_dim_v 100"),
+    ("head_dim_v", 520, UNSUPPORTED, "head_dim_v 520"),
     ("dtype", 7, UNSUPPORTED, "dtype"),
     ("mask", 3, UNSUPPORTED, "mask"),
     ("mask", -1, UNSUPPORTED, "mask"),
-    ("head_dim", 96, UNSUPPORTED, "head_dim 96"),
+    ("head_dim", 100, UNSUPPORTED, "head_dim 100"),
+    ("head_dim", 4, UNSUPPORTED, "head_dim 4"),
+    ("head_dim", 520, UNSUPPORTED, "head_dim 520"),
     ("head_dim", 0, INVALID, "head_dim"),
     ("heads_q", 3, INVALID, "multiple"),
     ("heads_kv", 0, INVALID, "head counts"),
@@ -208,7 +212,7 @@ def test_empty_batch_is_a_no_op(L):
 
 def test_last_error_is_thread_local(L):
     import threading
-    p = dense_problem(d=96)
+    p = dense_problem(d=100)
     fwd(L, p)
     mine = L.attn_last_error().decode()
     other = {}
@@ -234,11 +238,12 @@ def test_binding_rejects_host_tensors(lib_path):
 
 
 def test_problem_struct_layout():
-    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3], window_left + reserved (int32)
+    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3], window_left + head_dim_v (int32)
     assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24 + 8
     assert B.AttnProblem.cu_seqlens_q.offset == 40
     assert B.AttnProblem.q_stride.offset == 72
     assert B.AttnProblem.window_left.offset == 168
+    assert B.AttnProblem.head_dim_v.offset == 172
 
 
 def test_window_needs_a_causal_mask(L):
@@ -267,7 +272,8 @@ def test_merge_declines(L):
     expect(L, merge(L, p, n=0), INVALID, "n_parts")
     expect(L, merge(L, p, n=9), INVALID, "n_parts")
     bad = dense_problem(d=96)
-    expect(L, merge(L, bad), UNSUPPORTED, "head_dim")
+    bad.head_dim_v = 100
+    expect(L, merge(L, bad), UNSUPPORTED, "head_dim_v")
     bad = dense_problem()
     bad.dtype = 5
     expect(L, merge(L, bad), UNSUPPORTED, "dtype")
@@ -293,3 +299,26 @@ def test_merge_empty_is_a_no_op(L):
     assert merge(L, dense_problem(sq=0, skv=0)) == OK
     # exact aliasing of an output with a part is accepted (nothing to launch here)
     assert merge(L, dense_problem(b=0), o=Q, lse=DO) == OK
+
+
+def test_head_dims_that_are_multiples_of_8_are_accepted(L):
+    # validation only: the empty batch returns OK after every check and before any launch
+    for d, dv in [(8, 0), (96, 0), (192, 128), (264, 0), (504, 512), (512, 8), (40, 328)]:
+        p = dense_problem(b=0, d=d)
+        p.head_dim_v = dv
+        assert fwd(L, p) == OK, (d, dv, L.attn_last_error())
+        assert bwd(L, p) == OK, (d, dv, L.attn_last_error())
+
+
+def test_extents_use_each_tensors_head_dim(L):
+    # O of a (64, 512) problem is 8x wider than Q: an O that would overlap K only at its wide width is refused,
+    # and the same placement with a symmetric problem passes
+    p = dense_problem(b=1, sq=256, skv=256, hq=4, hkv=2, d=64)
+    p.head_dim_v = 512
+    p.o_stride[:] = (256 * 4 * 512, 4 * 512, 512)
+    p.v_stride[:] = (256 * 2 * 512, 2 * 512, 512)
+    q_bytes = 256 * 4 * 64 * 2
+    o_bytes_wide = 256 * 4 * 512 * 2
+    k_addr = O + q_bytes + 4096          # past a D=64 O, inside a D=512 O
+    assert k_addr < O + o_bytes_wide
+    expect(L, fwd(L, p, k=k_addr), OVERLAP, "o overlaps an input")

@@ -78,6 +78,7 @@ FULL_UNITS = {
     "cp_share_d256": [(0, 6)],
     "cp_share_d512": [(0, 3)],
     "window_d256": [(0, 2)],
+    "asym_d192": [(0, 11)],
 }
 
 

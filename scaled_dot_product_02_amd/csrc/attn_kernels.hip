@@ -526,7 +526,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
                         (s.wl < 0 || kv0 + BN - 1 >= qw0 + delta - s.wl);  // same for both waves of a pair
     const int kx = opaque(kkey), vx0 = opaque(vkey[0]), vx1 = opaque(vkey[1]);
     v16f sacc = v16f{};
-    if (active) {
+    if (active && (!PAD || hf * DH < s.dqk)) {  // a half of D wholly past D_qk adds 0 to S
 #pragma unroll
       for (int kk = 0; kk < DH / 16; ++kk) {
         const v8s kf = lds_read16(ks, krow + ((16 * kk) ^ kx));
@@ -537,9 +537,13 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
         v4f t4 = {sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
         *reinterpret_cast<v4f*>(mine + (q4 * 64 + lane) * 4) = t4;
       }
+    } else if (active) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) *reinterpret_cast<v4f*>(mine + (q4 * 64 + lane) * 4) = v4f{};
     }
     __syncthreads();
     if (!active) continue;
+    if (PAD && hf * DH >= s.dv) continue;  // all of this wave's O columns lie past D_v: nothing to compute
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const v4f t4 = *reinterpret_cast<const v4f*>(other + (q4 * 64 + lane) * 4);

@@ -30,7 +30,6 @@ typedef float v16f __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -99,18 +98,34 @@ __device__ __forceinline__ v8s cat44(v4s a, v4s b) {
   return r;
 }
 
-// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4). The LDS destination is
-// wave-uniform: lane l's 16 bytes land at lds_wave_base + 16*l.
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_cvoid*)g, (lds_void*)lds_wave_base, 16, 0, 0);
+// Direct HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4, scalar-base form): lane l
+// reads base + off (base wave-uniform, off a 32-bit per-lane byte offset) and its 16 bytes land at
+// lds_wave_base + 16*l (wave-uniform, passed in M0).
+//
+// Issued through inline asm on purpose. The compiler's wait-count pass models this instruction as
+// a flat access to both global memory and LDS; while one is outstanding it turns every later LDS
+// dependency into a full drain (s_waitcnt lgkmcnt(0), and vmcnt(0) before transpose reads), so the
+// K-fragment reads of a tile could not run ahead of their MFMAs and each tile's P*V waited for the
+// next tile's copy to land. The kernels order the copies themselves: every wave waits for its own
+// copies (wait_vmem) before the barrier that hands a stage to the readers, and a stage is
+// overwritten only after the barrier that ends its reads. vmcnt completes in issue order, so the
+// compiler's own waits for other loads stay correct (copies it does not know about only make them
+// more conservative).
+__device__ __forceinline__ void dma16(const void* base, unsigned off, void* lds_wave_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0));
 }
 // Same with 4 bytes per lane (lane l's dword lands at lds_wave_base + 4*l).
-__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_cvoid*)g, (lds_void*)lds_wave_base, 4, 0, 0);
+__device__ __forceinline__ void dma4(const void* base, unsigned off, void* lds_wave_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(m0));
 }
 
-// Wait until this wave's outstanding vector-memory loads (including LDS DMA) have landed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until this wave's outstanding vector-memory loads (including LDS DMA) have landed: s_waitcnt
+// with vmcnt = 0 and expcnt / lgkmcnt at their maxima (no wait on those). A real s_waitcnt, not inline
+// asm, so that the compiler's wait-count tracking sees it (loads issued before it need no further
+// wait after it).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // LDS tile rows are stored with their 16-byte chunks permuted: physical chunk = logical chunk ^
 // sw_key(row). For D >= 128 (16+ chunks per row) the key is the row's low 4 bits, bit-permuted

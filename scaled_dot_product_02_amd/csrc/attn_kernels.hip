@@ -149,8 +149,8 @@ struct TileDma {
       } else {
         offsets(lane, i, last, xb, yb);
       }
-      if (!PAD || ((xm >> i) & 1u)) dma16((const char*)xt + xb, xs + (slot0 + i * 64) * 8);
-      if (!PAD || ((ym >> i) & 1u)) dma16((const char*)yt + yb, ys + (slot0 + i * 64) * 8);
+      if (!PAD || ((xm >> i) & 1u)) dma16(xt, xb, xs + (slot0 + i * 64) * 8);
+      if (!PAD || ((ym >> i) & 1u)) dma16(yt, yb, ys + (slot0 + i * 64) * 8);
     }
   }
 };
@@ -736,8 +736,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
     float* rss = l2s + 64;
     dma.copy(ld.qp, ld.op, sq.sq - 1 - qs0, qs, dos);
     const int r = min(qs0 + lane, sq.sq - 1);
-    if (w == 0) dma4(ld.l2 + r, l2s);
-    if (w == 1) dma4(ld.rs + r, rss);
+    if (w == 0) dma4(ld.l2, 4u * r, l2s);
+    if (w == 1) dma4(ld.rs, 4u * r, rss);
     ld.next();
   };
 
@@ -1104,8 +1104,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     float* rss = l2s + 64;
     dma.copy(ld.qp, ld.op, sq.sq - 1 - qs0, qs, dos);
     const int r = min(qs0 + lane, sq.sq - 1);
-    if (w == 0) dma4(ld.l2 + r, l2s);
-    if (w == 1) dma4(ld.rs + r, rss);
+    if (w == 0) dma4(ld.l2, 4u * r, l2s);
+    if (w == 1) dma4(ld.rs, 4u * r, rss);
     ld.next();
   };
 

@@ -35,10 +35,10 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
 # source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
 TRAFFIC = {
-    ("dense_d128", "bwd_dkdv"): {"src_sha1": "beccd0513e32", "bytes": 697622702},
-    ("dense_d128", "fwd"): {"src_sha1": "beccd0513e32", "bytes": 806544378},
-    ("dense_d128", "bwd_dq"): {"src_sha1": "beccd0513e32", "bytes": 765277135},
-    ("dense_d128", "bwd_pre"): {"src_sha1": "beccd0513e32", "bytes": 159437553},
+    ("dense_d128", "bwd_dkdv"): {"src_sha1": "d79689a2fcef", "bytes": 691836008},
+    ("dense_d128", "fwd"): {"src_sha1": "d79689a2fcef", "bytes": 864616016},
+    ("dense_d128", "bwd_dq"): {"src_sha1": "d79689a2fcef", "bytes": 849919770},
+    ("dense_d128", "bwd_pre"): {"src_sha1": "d79689a2fcef", "bytes": 159437761},
 }
 
 
@@ -104,7 +104,7 @@ def flop_per_pair(w):
     return {"fwd": 2.0 * (dqk + dv), "bwd": 6.0 * dqk + 4.0 * dv, "bwd_dkdv": 4.0 * (dqk + dv), "bwd_dq": 2.0 * dqk}
 
 
-def cpu_baseline(w, x, budget_s=12.0, max_units=6):
+def cpu_baseline(w, x, budget_s=15.0, max_units=16):
     """Time the float64 oracle (forward + backward) on whole (sequence, kv-head) units."""
     import numpy as np
     from oracle import MASK_CAUSAL_BR, MASK_CAUSAL_TL, MASK_NONE, sdpa_bwd, sdpa_fwd

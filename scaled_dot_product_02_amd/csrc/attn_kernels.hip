@@ -665,8 +665,8 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 // Backward dK/dV pass. Workgroup = 4 waves = BKV = 64*KB keys of one (sequence, kv-head); wave w
 // owns 16*KB keys whose K and V fragments stay in VGPRs. It loops over every q-head of the GQA
-// group and every 32-row query tile that sees its keys; Q, dO, lse2 and D of the tile stream
-// through LDS. With 16x16x32 MFMAs:
+// group and every query tile that sees its keys (64 rows for D <= 128, computed as 32-row halves
+// under one barrier, else 32); Q, dO, lse2 and D of the tile stream through LDS. With 16x16x32 MFMAs:
 //   S = Q K^T, dP = dO V^T   (A = Q / dO rows from LDS, B = K / V fragments): lane = key
 //   P = exp2(S*c - lse2), dS = P (dP - D)
 //   dV += P^T dO, dK += dS^T Q  (A = the P / dS accumulators as they are, B = dO / Q by transpose
@@ -866,7 +866,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------------------------------
 // Backward dQ pass. Workgroup = 4 waves = 64*QB query rows of one (sequence, q-head); wave w owns
-// 16*QB rows whose Q and dO fragments stay in VGPRs. K/V tiles of 32 keys stream through LDS.
+// 16*QB rows whose Q and dO fragments stay in VGPRs. K/V tiles (64 or 32 keys, see BK) stream
+// through LDS.
 //   S^T = K Q^T, dP^T = V dO^T  (A = K / V rows from LDS, B = Q / dO fragments): lane = query
 //   P = exp2(S*c - lse2), dS = P (dP - D)            (lse2, D are per-lane scalars)
 //   dQ += dS K                  (A = the dS accumulators, B = K by transpose reads)

@@ -144,3 +144,36 @@ def test_headdim_merge_split_identity(dims):
     mo, ml = oracle_merge([p1[0], p2[0]], [lse_like_o(p1[1], False), lse_like_o(p2[1], False)])
     np.testing.assert_allclose(mo, ro, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse_like_o(rl, False), ml, rtol=0, atol=1e-12)
+
+
+def _padded(t, width):
+    """t with zero columns appended up to width (a new contiguous tensor)."""
+    out = torch.zeros(t.shape[:-1] + (width,), dtype=t.dtype, device=t.device)
+    out[..., : t.shape[-1]] = t
+    return out
+
+
+@pytest.mark.parametrize("dims,full", [((96, 96), 128), ((72, 40), 128), ((192, 128), 256), ((136, 200), 256),
+                                       ((264, 264), 512), ((320, 128), 512)], ids=lambda x: str(x))
+@pytest.mark.parametrize("mask", ["none", "causal_br"])
+def test_narrow_head_equals_the_full_width_kernel_on_zero_padded_tensors(dims, full, mask):
+    """Regression by behaviour: the padded instance must compute exactly what the full-width instance
+    computes on tensors that the caller padded with zero columns (the same products and sums in the same
+    order; zero columns add exact zeros), bit for bit on the real columns, with the same scale."""
+    dqk, dv = dims
+    w = small(f"hdeq_{dqk}_{dv}_{mask}", batch=2, hq=4, hkv=2, sq=150, skv=230, d=dqk, dv=dv, dtype="bf16",
+              mask=mask, seed=17)
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = sd.attn_fwd(q, k, v, mask=mask, scale=w.scale)
+    dq, dk, dvv = sd.attn_bwd(q, k, v, o, do, lse, mask=mask, scale=w.scale)
+    qp, kp, vp, dop = _padded(q, full), _padded(k, full), _padded(v, full), _padded(do, full)
+    op, lsep = sd.attn_fwd(qp, kp, vp, mask=mask, scale=w.scale)
+    dqp, dkp, dvp = sd.attn_bwd(qp, kp, vp, op, dop, lsep, mask=mask, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lsep)
+    assert torch.equal(o, op[..., :dv])
+    assert torch.equal(dq, dqp[..., :dqk])
+    assert torch.equal(dk, dkp[..., :dqk])
+    assert torch.equal(dvv, dvp[..., :dv])

@@ -12,6 +12,7 @@ Two kinds of cases:
 Acceptance is in parity_util.compare.
 """
 
+import dataclasses
 import pytest
 import torch
 
@@ -130,3 +131,18 @@ def test_window_packed(d, mask, wl, lens):
               seqlens=lq, seqlens_kv=lk, window_left=wl)
     ok, msgs = run_and_check(w)
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+@pytest.mark.parametrize("mask", ["causal_tl", "causal_br"])
+def test_window_wider_than_every_row_is_the_causal_result_bitwise(d, mask):
+    """Regression by behaviour: a window that reaches every row's first key (W >= Skv + |Skv - Sq|) must
+    take the same tiles and elements as no window at all, so forward and backward agree bit for bit."""
+    sq, skv = 200, 333
+    w = small(f"widewin_{d}_{mask}", batch=1, hq=4, hkv=2, sq=sq, skv=skv, d=d, dtype="bf16", mask=mask, seed=23)
+    x = make_inputs(w)
+    a = gpu_run(w, x)
+    wide = dataclasses.replace(w, window_left=skv + abs(skv - sq))
+    b = gpu_run(wide, x)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n

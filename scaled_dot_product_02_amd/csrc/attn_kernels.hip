@@ -550,23 +550,32 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[4 * q4 + i] += t4[i];
     }
-    // Branch-free mask (a per-element branch here doubles the live S values and spills): key
-    // kv0 + 8(jr/4) + 4hh + jr%4 is allowed iff its offset 8(jr/4) + jr%4 <= lim - kv0 - 4hh.
-    const int lim = (s.mask != 0 ? min(sq.skv - 1, qi + delta) : sq.skv - 1) - kv0 - 4 * hh;
-    const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);  // window start
+    // Mask, one branch per tile (the same for both waves of a pair): key kv0 + 8(jr/4) + 4hh + jr%4 is
+    // allowed iff its offset 8(jr/4) + jr%4 lies in [lo, lim] (relative to kv0 + 4hh).
+    const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta) ||
+                           (s.wl >= 0 && kv0 < qw0 + 31 + delta - s.wl);
     float mt = -__builtin_inff();
+    if (need_mask) {
+      // (opaque: the index arithmetic stays inside the branch instead of being hoisted onto every tile)
+      const int lim = opaque((s.mask != 0 ? min(sq.skv - 1, qi + delta) : sq.skv - 1) - kv0 - 4 * hh);
+      const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);  // window start
 #pragma unroll
-    for (int jr = 0; jr < 16; ++jr) {
-      const int off = 8 * (jr >> 2) + (jr & 3);
-      const float x = (off <= lim && off >= lo) ? sacc[jr] : -__builtin_inff();
-      sacc[jr] = x;
-      mt = fmaxf(mt, x);
+      for (int jr = 0; jr < 16; ++jr) {
+        const int off = 8 * (jr >> 2) + (jr & 3);
+        const float x = (off <= lim && off >= lo) ? sacc[jr] : -__builtin_inff();
+        sacc[jr] = x;
+        mt = fmaxf(mt, x);
+      }
+    } else {
+#pragma unroll
+      for (int jr = 0; jr < 16; ++jr) mt = fmaxf(mt, sacc[jr]);
     }
     const float m_new = pair32_max(mt) * c;
-    {  // branch-free form of the lazy rescale (alpha = 1 unless some row of the wave needs it)
-      const bool need = wave_any(m_new > m_ref + kRescaleThreshold);
-      const float ref = need ? fmaxf(m_ref, m_new) : m_ref;
-      const float alpha = (!need || ref == -__builtin_inff()) ? (need ? 0.f : 1.f) : fast_exp2(m_ref - ref);
+    // lazy rescale (rare; wave-uniform, and the same in both waves of a pair, which hold the same S)
+    if (wave_any(m_new > m_ref + kRescaleThreshold)) {
+      const float ref = fmaxf(m_ref, m_new);
+      // 0 when m_ref = -inf; rows still without any key keep ref = -inf (O and l are 0 there)
+      const float alpha = ref == -__builtin_inff() ? 0.f : fast_exp2(m_ref - ref);
       m_ref = ref;
       l_run *= alpha;
 #pragma unroll
@@ -1153,19 +1162,22 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
         for (int qb = 0; qb < 2; ++qb) {
           const v4f l2 = *reinterpret_cast<const v4f*>(l2s + 16 * qb + 4 * G);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float p = fast_exp2(sv[qb][i] * s.scale_log2 - l2[i]);
-            if (need_mask) {
-              const int q = qs0 + 16 * qb + 4 * G + i;
-              const int key = kw0 + l16;
-              const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta) &&
-                             (s.wl < 0 || key >= q + delta - s.wl);
-              p = ok ? p : 0.f;
-            }
-            sv[qb][i] = p;
-          }
-          *reinterpret_cast<v4f*>(pbuf + (qb * 64 + lane) * 4) = sv[qb];
+          for (int i = 0; i < 4; ++i) sv[qb][i] = fast_exp2(sv[qb][i] * s.scale_log2 - l2[i]);
         }
+        if (need_mask) {  // one branch per tile (a test inside the unrolled loop branches per element)
+          const int ql = opaque(qs0 + 4 * G), key = opaque(kw0 + l16);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int q = ql + 16 * qb + i;
+              const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta) &&
+                              (s.wl < 0 || key >= q + delta - s.wl);
+              sv[qb][i] = ok ? sv[qb][i] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) *reinterpret_cast<v4f*>(pbuf + (qb * 64 + lane) * 4) = sv[qb];
       }
     }
     __syncthreads();
@@ -1306,16 +1318,18 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float p = fast_exp2(st[kb][i] * s.scale_log2 - l2);
-            if (need_mask) {
-              const int q = qw0 + l16;
-              const int key = kv0 + 16 * kb + 4 * G + i;
+          for (int i = 0; i < 4; ++i) st[kb][i] = fast_exp2(st[kb][i] * s.scale_log2 - l2);
+        if (need_mask) {  // one branch per tile (a test inside the unrolled loop branches per element)
+          const int q = opaque(qw0 + l16), kl = opaque(kv0 + 4 * G);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kl + 16 * kb + i;
               const bool ok = key < sq.skv && (s.mask == 0 || key <= q + delta) && (s.wl < 0 || key >= q + delta - s.wl);
-              p = ok ? p : 0.f;
+              st[kb][i] = ok ? st[kb][i] : 0.f;
             }
-            st[kb][i] = p;
-          }
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) *reinterpret_cast<v4f*>(mine + (kb * 64 + lane) * 4) = st[kb];

@@ -9,13 +9,17 @@ Credited FLOPs (algorithmic, exact allowed-pair counts): forward 4*D per allowed
 (query, key) pair and q-head, backward 10*D (S recompute, dV, dP, dK, dQ). The
 value is (F_fwd + F_bwd) / step time. HIP events bracket every launch inside the
 timed region; the kernel with the largest per-step time is reported under
-"roofline" with its own algorithmic FLOPs per launch (forward 4D, dK/dV pass 8D,
-dQ pass 2D per pair, which sum to the 14D credited per step; the dQ pass's second
-S/dP recompute is not credited) against the dense bf16/fp16 MFMA peak of 2.5 PFLOP/s.
+"roofline". Each kernel is placed on the roofline by its algorithmic FLOPs per launch
+(forward 4D, dK/dV pass 8D, dQ pass 2D per pair, which sum to the 14D credited per
+step; the dQ pass's second S/dP recompute is not credited) over its compulsory HBM
+bytes: below the balance point 2.5 PFLOP/s / 8 TB/s it is HBM-bound and "achieved"
+is compulsory bytes per second against 8 TB/s, else MFMA-bound and "achieved" is
+algorithmic FLOP/s against 2.5 PFLOP/s ("kernel_roofline" lists all four).
 "cpu_baseline" times the float64 CPU oracle on a bounded sample of the same
 workload. The default run also reports, under "extra", the D=512 workload and
 attn_merge (two forward results combined, the ring step) on the dense D=128
-query side, the latter against the HBM peak. Prints one JSON line on stdout;
+query side, the latter against the HBM peak, and the HBM-bound short-sequence
+workload (B128 S256 D128). Prints one JSON line on stdout;
 diagnostics go to stderr.
 """
 
@@ -102,6 +106,44 @@ def flop_per_pair(w):
     is executed but not credited)."""
     dqk, dv = w.d, w.d_v
     return {"fwd": 2.0 * (dqk + dv), "bwd": 6.0 * dqk + 4.0 * dv, "bwd_dkdv": 4.0 * (dqk + dv), "bwd_dq": 2.0 * dqk}
+
+
+def compulsory_bytes(w, x, nrows):
+    """Bytes each kernel must move to or from HBM at least: its inputs read once, its outputs written once.
+
+    forward   Q, K, V read; O, LSE written
+    pre       O, dO, LSE read; D and LSE*log2(e) written (fp32)
+    dK/dV     Q, dO, K, V, D, LSE*log2(e) read; dK, dV written
+    dQ        Q, dO, K, V, D, LSE*log2(e) read; dQ written
+    """
+    el = 2  # bf16 / fp16
+    nkv = sum(x["seqlens_kv"]) if w.packed else w.batch * w.skv
+    q, o = nrows * w.hq * w.d * el, nrows * w.hq * w.d_v * el
+    k, v = nkv * w.hkv * w.d * el, nkv * w.hkv * w.d_v * el
+    row = nrows * w.hq * 4
+    return {"fwd": q + k + v + o + row, "bwd_pre": 2 * o + row + 2 * row,
+            "bwd_dkdv": q + o + k + v + 2 * row + k + v, "bwd_dq": q + o + k + v + 2 * row + q}
+
+
+def kernel_roofline(w, x, nrows, pairs, kern_ms):
+    """Roofline of each kernel: bound by HBM when its algorithmic FLOPs per compulsory byte are below
+    the chip's balance point (peak FLOP/s over peak bytes/s), else by the matrix cores."""
+    fp = flop_per_pair(w)
+    nbytes = compulsory_bytes(w, x, nrows)
+    balance = PEAK_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    out = {}
+    for n, ms in kern_ms.items():
+        flops = fp.get(n, 0) * pairs
+        if flops / nbytes[n] < balance:
+            ach = nbytes[n] / (ms * 1e-3) / 1e9
+            out[n] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                      "bytes": nbytes[n]}
+        else:
+            ach = flops / (ms * 1e-3) / 1e12
+            out[n] = {"bound": "mfma", "achieved": ach, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": ach / PEAK_TFLOPS}
+        out[n]["flop_per_byte"] = flops / nbytes[n]
+    return out
 
 
 def cpu_baseline(w, x, budget_s=15.0, max_units=16):
@@ -232,7 +274,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the informational D=512 line")
+    ap.add_argument("--no-extra", action="store_true", help="skip the informational D=512, merge and short-sequence lines")
     ap.add_argument("--merge-only", action="store_true",
                     help="only time attn_merge of two forward results (dense_d128 query side) and print its line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -271,15 +313,9 @@ def main():
     f_fwd, f_bwd = fp["fwd"] * pairs, fp["bwd"] * pairs
     value = (f_fwd + f_bwd) / (r["ms_step"] * 1e-3) / 1e12
     km = r["kern_ms"]
-    algo_flops = {n: fp[n] * pairs for n in ("fwd", "bwd_dkdv", "bwd_dq")}
-    pre_bytes = r["nrows"] * w.hq * (2 * w.d_v * 2 + 4 + 8)
+    kroof = kernel_roofline(w, r["x"], r["nrows"], pairs, km)
     dom = max(km, key=km.get)
-    if dom == "bwd_pre":
-        ach = pre_bytes / (km[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
-    else:
-        ach = algo_flops[dom] / (km[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_TFLOPS}
+    roof = {kk: kroof[dom][kk] for kk in ("bound", "achieved", "peak", "unit", "frac")}
     roof["kernel"] = dom
     roof["avg_launch_ms"] = km[dom]
     roof["traffic"] = traffic_for(w.name, dom)
@@ -301,6 +337,8 @@ def main():
                 "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},
         "kernel_ms": {n: round(t, 4) for n, t in km.items()},
         "roofline": {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in roof.items()},
+        "kernel_roofline": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in e.items()}
+                            for n, e in kroof.items()},
     }
     if not args.no_extra and w.name == "dense_d128":
         w2 = WORKLOADS["dense_d512"]
@@ -312,6 +350,13 @@ def main():
                                        "ms_per_step": round(r2["ms_step"], 4),
                                        "kernel_ms": {n: round(t, 4) for n, t in km2.items()}},
                         "merge": merge_measure(w)}
+        w3 = WORKLOADS["short_d128"]
+        r3 = run(w3, max(5, args.steps // 3), 3)
+        kr3 = kernel_roofline(w3, r3["x"], r3["nrows"], r3["pairs"], r3["kern_ms"])
+        out["extra"]["short_d128"] = {
+            "ms_per_step": round(r3["ms_step"], 4), "kernel_ms": {n: round(t, 4) for n, t in r3["kern_ms"].items()},
+            "kernel_roofline": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in e.items()}
+                                for n, e in kr3.items()}}
     if not args.no_cpu_baseline:
         log("timing the float64 CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, r["x"])

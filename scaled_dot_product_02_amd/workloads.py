@@ -89,6 +89,10 @@ WORKLOADS = {
     # at the dense D=128 shape; it runs on the D=256 kernels with padded columns
     "asym_d192": Workload("asym_d192", batch=2, hq=16, hkv=16, sq=8192, skv=8192, d=192, dv=128, dtype="bf16",
                           mask="causal_tl", seed=6, note="B2 H16/16 S8192 Dqk192/Dv128 bf16 causal top-left"),
+    # many short sequences: every pass moves more bytes per FLOP than the chip's balance point
+    # (2.5 PFLOP/s / 8 TB/s), so HBM bandwidth, not the matrix cores, bounds it
+    "short_d128": Workload("short_d128", batch=128, hq=16, hkv=16, sq=256, skv=256, d=128, dtype="bf16",
+                           mask="causal_tl", seed=7, note="B128 H16/16 S256 D128 bf16 causal top-left (HBM-bound)"),
 }
 
 

@@ -80,6 +80,7 @@ FULL_UNITS = {
     "cp_share_d512": [(0, 3)],
     "window_d256": [(0, 2)],
     "asym_d192": [(0, 11)],
+    "short_d128": [(0, 0), (63, 7), (127, 15)],
 }
 
 

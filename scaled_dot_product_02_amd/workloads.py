@@ -129,6 +129,16 @@ def make_inputs(w: Workload, with_do: bool = True):
                 max_seqlen_q=max(lq) if lq else 0, max_seqlen_kv=max(lk) if lk else 0)
 
 
+def draw_device(shape, seed, dtype, device="cuda:0"):
+    """N(0,1) in float32 from torch's seeded generator on the device, rounded to dtype: inputs too large
+    to draw on the host and copy up (the tests read back the slices they check)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    out = x.to(dtype)
+    del x
+    return out
+
+
 def small(name="small", *, batch=1, hq=2, hkv=2, sq=64, skv=64, d=64, dtype="bf16", mask="causal_tl", seed=0,
           seqlens=None, seqlens_kv=None, window_left=-1, dv=0):
     """A test-sized workload with the same recipe."""

@@ -8,7 +8,8 @@ exactly what attn_bwd runs), each a single kernel launch on the current stream.
 Credited FLOPs (algorithmic, exact allowed-pair counts): forward 4*D per allowed
 (query, key) pair and q-head, backward 10*D (S recompute, dV, dP, dK, dQ). The
 value is (F_fwd + F_bwd) / step time. HIP events bracket every launch inside the
-timed region; the kernel with the largest per-step time is reported under
+timed region (mean, median and minimum per kernel); the kernel with the largest
+per-step time is reported under
 "roofline". Each kernel is placed on the roofline by its algorithmic FLOPs per launch
 (forward 4D, dK/dV pass 8D, dQ pass 2D per pair, which sum to the 14D credited per
 step; the dQ pass's second S/dP recompute is not credited) over its compulsory HBM
@@ -227,12 +228,16 @@ def run(w, steps, warmup, want_events=True):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    kern_ms = {}
+    kern_ms, kern_med, kern_min = {}, {}, {}
     if evs:
         for j, n in enumerate(names):
-            kern_ms[n] = sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+            per = sorted(e[j].elapsed_time(e[j + 1]) for e in evs)
+            kern_ms[n] = sum(per) / steps
+            kern_med[n] = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+            kern_min[n] = per[0]
     pairs = allowed_pairs(x["seqlens_q"], x["seqlens_kv"], w.mask, w.window_left) * w.hq
-    return dict(x=x, ms_step=ms_step, kern_ms=kern_ms, pairs=pairs, nrows=p.total_q if w.packed else w.batch * w.sq)
+    return dict(x=x, ms_step=ms_step, kern_ms=kern_ms, kern_med=kern_med, kern_min=kern_min, pairs=pairs,
+                nrows=p.total_q if w.packed else w.batch * w.sq)
 
 
 def merge_measure(w, parts=2, steps=20, warmup=3):
@@ -336,6 +341,8 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},
         "kernel_ms": {n: round(t, 4) for n, t in km.items()},
+        "kernel_ms_median": {n: round(t, 4) for n, t in r["kern_med"].items()},
+        "kernel_ms_min": {n: round(t, 4) for n, t in r["kern_min"].items()},
         "roofline": {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in roof.items()},
         "kernel_roofline": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                             for n, e in kroof.items()},

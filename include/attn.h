@@ -91,7 +91,10 @@ typedef enum { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL_TL = 1, ATTN_MASK_CAUSAL_BR 
  * with every sequence length <= max_seqlen_q / max_seqlen_kv and a non-empty KV range wherever the
  * query range is non-empty. LSE is contiguous fp32 [total_q, Hq] (token-major).
  *
- * Row strides (sequence stride for dense, token stride for packed) must be below 2^24 elements.
+ * Row strides (sequence stride for dense, token stride for packed) must be below 2^24 elements,
+ * and batch * heads * ceil(max_seqlen / 64) must stay below 2^31 for the query side (heads_q) and
+ * the key side (heads_kv): one workgroup per tile of at least 64 rows or keys; beyond that the call
+ * is ATTN_E_UNSUPPORTED.
  * Grouped-query attention: q-head h reads kv-head h / (heads_q / heads_kv).
  * dQ/dK/dV use the strides of Q/K/V; dO uses the strides of O. */
 typedef struct attn_problem {

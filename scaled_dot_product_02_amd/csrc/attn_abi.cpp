@@ -101,6 +101,12 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (p->window_left >= 0 && p->mask == ATTN_MASK_NONE)
     return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
                 p->window_left);
+  // one workgroup per (sequence, head, tile) of at least 64 rows or keys: every grid must fit in 32 bits
+  const int64_t qgrid = (int64_t)p->batch * p->heads_q * (((int64_t)p->max_seqlen_q + 63) / 64);
+  const int64_t kgrid = (int64_t)p->batch * p->heads_kv * (((int64_t)p->max_seqlen_kv + 63) / 64);
+  if (qgrid > INT32_MAX || kgrid > INT32_MAX)
+    return fail(ATTN_E_UNSUPPORTED, "%lld query / %lld key tiles exceed the 32-bit launch grid", (long long)qgrid,
+                (long long)kgrid);
   const bool packed = p->cu_seqlens_q != nullptr;
   if (packed != (p->cu_seqlens_kv != nullptr))
     return fail(ATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_kv must both be set (packed) or both be NULL");

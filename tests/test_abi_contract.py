@@ -110,6 +110,7 @@ def test_null_problem(L):
     ("heads_q", 3, INVALID, "multiple"),
     ("heads_kv", 0, INVALID, "head counts"),
     ("batch", -1, INVALID, "batch"),
+    ("batch", 1 << 30, UNSUPPORTED, "launch grid"),
     ("scale", float("inf"), INVALID, "scale"),
     ("scale", float("nan"), INVALID, "scale"),
     ("scale", 0.0, UNSUPPORTED, "not positive"),

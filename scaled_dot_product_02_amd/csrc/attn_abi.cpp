@@ -102,11 +102,11 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
     return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
                 p->window_left);
   // one workgroup per (sequence, head, tile) of at least 64 rows or keys: every grid must fit in 32 bits
-  const int64_t qgrid = (int64_t)p->batch * p->heads_q * (((int64_t)p->max_seqlen_q + 63) / 64);
-  const int64_t kgrid = (int64_t)p->batch * p->heads_kv * (((int64_t)p->max_seqlen_kv + 63) / 64);
-  if (qgrid > INT32_MAX || kgrid > INT32_MAX)
-    return fail(ATTN_E_UNSUPPORTED, "%lld query / %lld key tiles exceed the 32-bit launch grid", (long long)qgrid,
-                (long long)kgrid);
+  // (units = batch * heads < 2^62 cannot overflow; the product with the tile count is tested by division)
+  const int64_t uq = (int64_t)p->batch * p->heads_q, uk = (int64_t)p->batch * p->heads_kv;
+  const int64_t tq = ((int64_t)p->max_seqlen_q + 63) / 64, tk = ((int64_t)p->max_seqlen_kv + 63) / 64;
+  if ((uq > 0 && tq > INT32_MAX / uq) || (uk > 0 && tk > INT32_MAX / uk))
+    return fail(ATTN_E_UNSUPPORTED, "batch x heads x tiles exceed the 32-bit launch grid");
   const bool packed = p->cu_seqlens_q != nullptr;
   if (packed != (p->cu_seqlens_kv != nullptr))
     return fail(ATTN_E_INVALID, "cu_seqlens_q and cu_seqlens_kv must both be set (packed) or both be NULL");
@@ -434,6 +434,9 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
       return fail(ATTN_E_INVALID, "total_q %lld out of range", (long long)p->total_q);
     in.nq = in.packed ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
     in.nkv = 0;
+    // at least 4 (row, head) pairs per workgroup: the grid fits in 32 bits
+    if (in.nq > (int64_t)INT32_MAX * 4 / p->heads_q)
+      return fail(ATTN_E_UNSUPPORTED, "rows x heads exceed the 32-bit launch grid");
     for (int i = 0; i < (in.packed ? 2 : 3); ++i) {
       if (p->o_stride[i] < 0) return fail(ATTN_E_INVALID, "o_stride[%d] is negative", i);
       if (p->o_stride[i] % 8)

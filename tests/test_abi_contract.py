@@ -284,6 +284,15 @@ def test_merge_declines(L):
     expect(L, merge(L, p, o=O + 8), ALIGN, "o")
     expect(L, merge(L, p, lse=LSE + 2), ALIGN, "lse")
     expect(L, merge(L, p, o_parts=[Q + 8, K]), ALIGN, "o_parts")
+    big = dense_problem(b=1 << 24, sq=1 << 10)  # 2^34 rows x 4 heads: past the 32-bit grid
+    expect(L, merge(L, big), UNSUPPORTED, "launch grid")
+
+
+def test_declines_grids_past_32_bits_without_overflowing(L):
+    # batch x heads x tiles far beyond 2^63 must still be declined cleanly (no 64-bit overflow)
+    p = dense_problem(b=(1 << 31) - 1, sq=(1 << 31) - 1, skv=(1 << 31) - 1, hq=1 << 30, hkv=1 << 30)
+    expect(L, fwd(L, p), UNSUPPORTED, "launch grid")
+    expect(L, bwd(L, p), UNSUPPORTED, "launch grid")
 
 
 def test_merge_overlap_rules(L):

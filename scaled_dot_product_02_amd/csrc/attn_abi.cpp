@@ -46,15 +46,23 @@ struct Info {
 // Byte extent [lo, hi) of a [seq, rows, heads, D] tensor described by strides (elements).
 struct Extent {
   uintptr_t lo = 0, hi = 0;
+  bool huge = false;  // spans more than kMaxExtent bytes (strides or sizes no allocation can have)
   bool empty() const { return hi <= lo; }
 };
+constexpr __int128 kMaxExtent = (__int128)1 << 62;
 
 Extent extent16(const void* base, const int64_t* st, bool packed, int64_t batch, int64_t rows, int64_t heads,
                 int64_t d) {
   Extent e;  // a NULL base still gets its size, so that check_ptr can reject it
   if (rows <= 0 || heads <= 0 || (!packed && batch <= 0)) return e;
-  int64_t last = (rows - 1) * (packed ? st[0] : st[1]) + (heads - 1) * (packed ? st[1] : st[2]) + (d - 1);
-  if (!packed) last += (batch - 1) * st[0];
+  // strides are non-negative (checked before); 128-bit arithmetic cannot overflow here
+  __int128 last = (__int128)(rows - 1) * (packed ? st[0] : st[1]) + (__int128)(heads - 1) * (packed ? st[1] : st[2]) +
+                  (d - 1);
+  if (!packed) last += (__int128)(batch - 1) * st[0];
+  if ((last + 1) * 2 > kMaxExtent) {
+    e.huge = true;
+    return e;
+  }
   e.lo = (uintptr_t)base;
   e.hi = e.lo + (uintptr_t)(last + 1) * 2;
   return e;
@@ -114,6 +122,9 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
     if (p->total_q < 0 || p->total_kv < 0) return fail(ATTN_E_INVALID, "negative total_q/total_kv");
     if (p->total_q > INT32_MAX || p->total_kv > INT32_MAX)
       return fail(ATTN_E_UNSUPPORTED, "packed totals beyond int32 offsets");
+    // every sequence is at most max_seqlen long, so the totals are at most batch times that
+    if (p->total_q > (int64_t)p->batch * p->max_seqlen_q || p->total_kv > (int64_t)p->batch * p->max_seqlen_kv)
+      return fail(ATTN_E_INVALID, "total_q / total_kv exceed batch x max_seqlen");
     if (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_kv, 4))
       return fail(ATTN_E_ALIGN, "cu_seqlens must be 4-byte aligned");
   }
@@ -148,12 +159,17 @@ Extent ext_q(const attn_problem_t* p, const void* base, const int64_t* st, bool 
 Extent ext_lse(const attn_problem_t* p, const float* lse, const Info& in) {
   Extent e;
   if (in.nq <= 0) return e;
+  if ((__int128)in.nq * p->heads_q * 4 > kMaxExtent) {
+    e.huge = true;
+    return e;
+  }
   e.lo = (uintptr_t)lse;
   e.hi = e.lo + (uintptr_t)(in.nq * p->heads_q) * 4;
   return e;
 }
 
 attn_status_t check_ptr(const void* ptr, const Extent& e, const char* name) {
+  if (e.huge) return fail(ATTN_E_UNSUPPORTED, "%s spans more than 2^62 bytes", name);
   if (e.empty()) return ATTN_OK;  // nothing is read or written through it
   if (!ptr) return fail(ATTN_E_INVALID, "%s is NULL", name);
   if (!aligned(ptr, 16)) return fail(ATTN_E_ALIGN, "%s is not 16-byte aligned", name);
@@ -257,6 +273,7 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
     if ((st = check_ptr(q, eq, "q")) || (st = check_ptr(k, ek, "k")) || (st = check_ptr(v, ev, "v")) ||
         (st = check_ptr(o, eo, "o")))
       return st;
+    if (el.huge) return fail(ATTN_E_UNSUPPORTED, "lse spans more than 2^62 bytes");
     if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
     if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
     const size_t need = attn_fwd_workspace_bytes(p);
@@ -324,6 +341,7 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
         (st = check_ptr(o, eo, "o")) || (st = check_ptr(d_o, edo, "d_o")) || (st = check_ptr(dq, edq, "dq")) ||
         (st = check_ptr(dk, edk, "dk")) || (st = check_ptr(dv, edv, "dv")))
       return st;
+    if (el.huge) return fail(ATTN_E_UNSUPPORTED, "lse spans more than 2^62 bytes");
     if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
     if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
     const size_t need = attn_bwd_workspace_bytes(p);
@@ -446,6 +464,7 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
     const Extent eo = ext_q(p, o, p->o_stride, false, in, dv), el = ext_lse(p, lse, in);
     attn_status_t st = check_ptr(o, eo, "o");
     if (st) return st;
+    if (el.huge) return fail(ATTN_E_UNSUPPORTED, "lse spans more than 2^62 bytes");
     if (!el.empty() && !lse) return fail(ATTN_E_INVALID, "lse is NULL");
     if (!el.empty() && !aligned(lse, 4)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
     if (overlaps(eo, el)) return fail(ATTN_E_OVERLAP, "o overlaps lse");

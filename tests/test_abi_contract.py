@@ -288,6 +288,21 @@ def test_merge_declines(L):
     expect(L, merge(L, big), UNSUPPORTED, "launch grid")
 
 
+def test_declines_extents_past_2_62_bytes(L):
+    # a batch stride no allocation can have: the extent is computed without overflow and refused
+    p = dense_problem()
+    p.q_stride[0] = 1 << 62
+    expect(L, fwd(L, p), UNSUPPORTED, "q spans more than 2^62 bytes")
+    expect(L, bwd(L, p), UNSUPPORTED, "q spans more than 2^62 bytes")
+
+
+def test_declines_packed_totals_beyond_batch_times_max(L):
+    p = packed_problem(tq=1000, nseq=4)
+    p.max_seqlen_q = 200  # 4 sequences of at most 200 tokens cannot hold 1000
+    expect(L, fwd(L, p), INVALID, "exceed batch x max_seqlen")
+    expect(L, bwd(L, p), INVALID, "exceed batch x max_seqlen")
+
+
 def test_declines_grids_past_32_bits_without_overflowing(L):
     # batch x heads x tiles far beyond 2^63 must still be declined cleanly (no 64-bit overflow)
     p = dense_problem(b=(1 << 31) - 1, sq=(1 << 31) - 1, skv=(1 << 31) - 1, hq=1 << 30, hkv=1 << 30)

@@ -3,8 +3,10 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_d128]
 
 One step is the whole hot path over one batch already resident in HBM: attn_fwd,
-then the three backward passes (attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq,
-exactly what attn_bwd runs), each a single kernel launch on the current stream.
+then the backward passes exactly as attn_bwd runs them, each a single kernel
+launch on the current stream: attn_bwd_dq_preprocess (the dQ pass with the
+preprocess folded in) and attn_bwd_dkdv for head dims up to 256,
+attn_bwd_preprocess, attn_bwd_dkdv and attn_bwd_dq for wider heads.
 Credited FLOPs (algorithmic, exact allowed-pair counts): forward 4*D per allowed
 (query, key) pair and q-head, backward 10*D (S recompute, dV, dP, dK, dQ). The
 value is (F_fwd + F_bwd) / step time. HIP events bracket every launch inside the
@@ -109,21 +111,28 @@ def flop_per_pair(w):
     return {"fwd": 2.0 * (dqk + dv), "bwd": 6.0 * dqk + 4.0 * dv, "bwd_dkdv": 4.0 * (dqk + dv), "bwd_dq": 2.0 * dqk}
 
 
+def fused_backward(w):
+    """Whether attn_bwd runs the dQ pass with the preprocess folded in (kernels up to head dim 256)."""
+    return max(w.d, w.d_v) <= 256
+
+
 def compulsory_bytes(w, x, nrows):
     """Bytes each kernel must move to or from HBM at least: its inputs read once, its outputs written once.
 
     forward   Q, K, V read; O, LSE written
     pre       O, dO, LSE read; D and LSE*log2(e) written (fp32)
     dK/dV     Q, dO, K, V, D, LSE*log2(e) read; dK, dV written
-    dQ        Q, dO, K, V, D, LSE*log2(e) read; dQ written
+    dQ        Q, dO, K, V, D, LSE*log2(e) read; dQ written; with the preprocess folded in, O and LSE
+              read and D, LSE*log2(e) written instead of read
     """
     el = 2  # bf16 / fp16
     nkv = sum(x["seqlens_kv"]) if w.packed else w.batch * w.skv
     q, o = nrows * w.hq * w.d * el, nrows * w.hq * w.d_v * el
     k, v = nkv * w.hkv * w.d * el, nkv * w.hkv * w.d_v * el
     row = nrows * w.hq * 4
+    dq = q + o + k + v + q + (o + row + 2 * row if fused_backward(w) else 2 * row)
     return {"fwd": q + k + v + o + row, "bwd_pre": 2 * o + row + 2 * row,
-            "bwd_dkdv": q + o + k + v + 2 * row + k + v, "bwd_dq": q + o + k + v + 2 * row + q}
+            "bwd_dkdv": q + o + k + v + 2 * row + k + v, "bwd_dq": dq}
 
 
 def kernel_roofline(w, x, nrows, pairs, kern_ms):
@@ -202,7 +211,11 @@ def run(w, steps, warmup, want_events=True):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wsf = torch.empty(max(sd.attn_fwd_workspace_bytes(p), 256), dtype=torch.uint8, device=dev)
     wsb = torch.empty(sd.attn_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    names = ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    # the launches attn_bwd makes: the dQ pass with the preprocess folded in, then dK/dV (head dims up
+    # to 256); preprocess, dK/dV, dQ for wider heads
+    fused = fused_backward(w)
+    names = ["fwd", "bwd_dq", "bwd_dkdv"] if fused else ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
+    seq = ["dq_preprocess", "dkdv"] if fused else ["preprocess", "dkdv", "dq"]
 
     def step(ev=None):
         def mark(i):
@@ -210,18 +223,15 @@ def run(w, steps, warmup, want_events=True):
                 ev[i].record()
         mark(0)
         sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, **kw)
-        mark(1)
-        sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=("preprocess",), **kw)
-        mark(2)
-        sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=("dkdv",), **kw)
-        mark(3)
-        sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=("dq",), **kw)
-        mark(4)
+        for i, pas in enumerate(seq):
+            mark(1 + i)
+            sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=(pas,), **kw)
+        mark(1 + len(seq))
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)] if want_events else None
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)] if want_events else None
     t0 = time.perf_counter()
     for i in range(steps):
         step(evs[i] if evs else None)
@@ -325,7 +335,7 @@ def main():
     roof["avg_launch_ms"] = km[dom]
     roof["traffic"] = traffic_for(w.name, dom)
     fwd_ms = km["fwd"]
-    bwd_ms = km["bwd_pre"] + km["bwd_dkdv"] + km["bwd_dq"]
+    bwd_ms = sum(t for n, t in km.items() if n != "fwd")
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 4), "higher_is_better": True, "scaling": "weak",

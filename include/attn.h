@@ -146,13 +146,17 @@ attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, co
                        const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
                        size_t ws_bytes, void* stream);
 
-/* The three passes attn_bwd runs, in this order, as separate calls with attn_bwd's arguments
- * (each validates the whole argument list the same way). The backward is defined by the method as
- * these steps: preprocess D = rowsum(dO * O) (and LSE in log2 units, +inf for rows with no key)
- * into the workspace, writing the error word for packed batches; the dK/dV pass, which writes dk
- * and dv; the dQ pass, which writes dq. dkdv and dq read what preprocess left in the same workspace
- * for the same problem and inputs, so they must follow it on the same stream (or after an event);
- * they are independent of each other. Splitting them lets a caller time or overlap the passes. */
+/* The passes of the backward as separate calls with attn_bwd's arguments (each validates the whole
+ * argument list the same way). The backward is defined by the method as these steps: preprocess
+ * D = rowsum(dO * O) (and LSE in log2 units, +inf for rows with no key) into the workspace, writing
+ * the error word for packed batches; the dK/dV pass, which writes dk and dv; the dQ pass, which
+ * writes dq. dkdv and dq read what preprocess left in the same workspace for the same problem and
+ * inputs, so they must follow it on the same stream (or after an event); they are independent of
+ * each other. attn_bwd_dq_preprocess is the dQ pass with the preprocess folded in (it writes the
+ * workspace's D and LSE rows for attn_bwd_dkdv, which must follow it): attn_bwd runs
+ * attn_bwd_dq_preprocess then attn_bwd_dkdv for head dims up to 256, and the three passes in the
+ * order preprocess, dkdv, dq for wider heads. Every split computes the same quantities (up to the
+ * summation order of D). Splitting them lets a caller time or overlap the passes. */
 attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* q, const void* k, const void* v,
                                   const void* o, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
                                   void* ws, size_t ws_bytes, void* stream);
@@ -162,6 +166,9 @@ attn_status_t attn_bwd_dkdv(const attn_problem_t* p, const void* q, const void* 
 attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
                           const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
                           size_t ws_bytes, void* stream);
+attn_status_t attn_bwd_dq_preprocess(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                                     const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                                     void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* Merge of attention results over disjoint key chunks: the combination step of the p2p (ring)
  * context-parallel mode, which shards the keys across steps (pull request 3527, section Scope), with

@@ -18,11 +18,13 @@ ABI_VERSION = 3
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_merge",
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess",
+            "attn_merge",
             "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
             "attn_abi_version")
 MERGE_MAX_PARTS = 8
-BWD_PASSES = {"all": "attn_bwd", "preprocess": "attn_bwd_preprocess", "dkdv": "attn_bwd_dkdv", "dq": "attn_bwd_dq"}
+BWD_PASSES = {"all": "attn_bwd", "preprocess": "attn_bwd_preprocess", "dkdv": "attn_bwd_dkdv", "dq": "attn_bwd_dq",
+              "dq_preprocess": "attn_bwd_dq_preprocess"}
 
 
 class AttnProblem(ctypes.Structure):
@@ -220,7 +222,9 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
 
     dO must have O's strides; dQ/dK/dV are allocated with Q/K/V's shapes (contiguous) unless given.
     ``passes`` lists the entry points to call in order: "all" (attn_bwd) or any of "preprocess",
-    "dkdv", "dq" (attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq, which share the workspace).
+    "dkdv", "dq", "dq_preprocess" (attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq /
+    attn_bwd_dq_preprocess, which share the workspace; "dq_preprocess" then "dkdv" is what
+    attn_bwd runs for head dims up to 256).
     """
     import torch
     _check_device(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv)

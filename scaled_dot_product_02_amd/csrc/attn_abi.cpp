@@ -385,7 +385,7 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     a.alse = lse_addr(p, in.packed);
     const int kt = sdpa::bwd_key_tile(inst);
     a.n_kvtiles = (p->max_seqlen_kv + kt - 1) / kt;
-    if (in.packed && (passes & sdpa::kPassPre)) {
+    if (in.packed && (passes & (sdpa::kPassPre | sdpa::kPassDqPre))) {
       const int e = sdpa::launch_validate_cu(a.s, stream);
       if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
     }
@@ -423,6 +423,12 @@ attn_status_t attn_bwd_dq(const attn_problem_t* p, const void* q, const void* k,
                           const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
                           size_t ws_bytes, void* stream) {
   return bwd_passes(sdpa::kPassDq, p, q, k, v, o, d_o, lse, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+attn_status_t attn_bwd_dq_preprocess(const attn_problem_t* p, const void* q, const void* k, const void* v,
+                                     const void* o, const void* d_o, const float* lse, void* dq, void* dk,
+                                     void* dv, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_passes(sdpa::kPassDqPre, p, q, k, v, o, d_o, lse, dq, dk, dv, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -78,8 +78,9 @@ struct MergeArgs {
 int instance_head_dim(int dqk, int dv);  // smallest of 64, 128, 256, 512 holding both, 0 if none
 int launch_validate_cu(const AttnShape& s, void* stream);
 int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream);
-// Backward passes selected by bit: 1 = preprocess, 2 = dK/dV pass, 4 = dQ pass.
-enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassAll = 7 };
+// Backward passes selected by bit: 1 = preprocess, 2 = dK/dV pass, 4 = dQ pass, 8 = the dQ pass with
+// the preprocess folded in (the same as 1 | 4). Preprocess and dQ together run fused for D <= 256.
+enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassDqPre = 8, kPassAll = 7 };
 int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream);
 int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
 int fwd_query_tile(int head_dim);

@@ -881,7 +881,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
 //   P = exp2(S*c - lse2), dS = P (dP - D)            (lse2, D are per-lane scalars)
 //   dQ += dS K                  (A = the dS accumulators, B = K by transpose reads)
 // ------------------------------------------------------------------------------------------
-template <int D, int QB, int MINW, typename T, bool PAD>
+// PRE: the pass also does the preprocess for its own rows (it holds their dO already): it loads O
+// beside dO, forms D = rowsum(dO * O) and LSE * log2(e), uses them and stores them for the dK/dV pass,
+// which then runs after it. Every query row of every head belongs to exactly one query tile.
+template <int D, int QB, int MINW, typename T, bool PAD, bool PRE = false>
 __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   // key tiles of BK = 64 (D <= 128) or 32 keys, processed as 32-key halves: a larger tile halves the
   // barriers, waits and copy issues per key at the same register use
@@ -927,8 +930,37 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
       qf[qb][kk] = ld_chunk<PAD>(qg + r * a.aq.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dqk);
       df[qb][kk] = ld_chunk<PAD>(dg + r * a.ao.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dv);
     }
-    l2[qb] = a.lse2[(int64_t)h * a.nrows + rowbase + r];
-    dr[qb] = a.rowsum[(int64_t)h * a.nrows + rowbase + r];
+    if constexpr (!PRE) {
+      l2[qb] = a.lse2[(int64_t)h * a.nrows + rowbase + r];
+      dr[qb] = a.rowsum[(int64_t)h * a.nrows + rowbase + r];
+    }
+  }
+  if constexpr (PRE) {
+    // lanes l16, l16 + 16, l16 + 32, l16 + 48 hold a row's dO between them (chunks 32kk + 8G)
+    const us* og = (const us*)a.o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h * a.ao.head;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int q = qw0 + 16 * qb + l16;
+      const int64_t r = min(q, sq.sq - 1);
+      float part = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const v8s o8 = ld_chunk<PAD>(og + r * a.ao.row + 32 * kk + 8 * G, 32 * kk + 8 * G, s.dv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part += to_f32<T>(o8[i]) * to_f32<T>(df[qb][kk][i]);
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      dr[qb] = part;
+      const int64_t lofs = packed ? (rowbase + r) * a.alse.row + (int64_t)h * a.alse.head
+                                  : (int64_t)b * a.alse.batch + r * a.alse.row + (int64_t)h * a.alse.head;
+      const float l = a.lse[lofs];
+      l2[qb] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+      if (G == 0 && q < sq.sq) {
+        a.rowsum[(int64_t)h * a.nrows + rowbase + r] = dr[qb];
+        a.lse2[(int64_t)h * a.nrows + rowbase + r] = l2[qb];
+      }
+    }
   }
   v4f dq[QB][D / 16];
 #pragma unroll
@@ -1467,10 +1499,31 @@ static int fwd_t(const FwdArgs& a, hipStream_t st) {
 template <int D, typename T, bool PAD>
 static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
   // Launches with an empty grid are skipped (e.g. no query rows: only dK = dV = 0 remain to write).
+  // With D <= 256, a request for both the preprocess and the dQ pass (attn_bwd, or the fused pass on
+  // its own) runs the dQ pass with the preprocess folded in, before the dK/dV pass that reads its
+  // D and LSE * log2(e): two launches instead of three. D = 512 keeps the three passes.
   constexpr int RPB = 256 / (D / 8);
   const int64_t rows = a.nrows * a.s.hq;
   hipError_t e = hipSuccess;
-  if ((passes & kPassPre) && rows > 0) {
+  if (passes & kPassDqPre) passes |= kPassPre | kPassDq;
+  const bool fuse = D <= 256 && (passes & kPassPre) && (passes & kPassDq);
+  auto run_dq = [&](bool pre) {
+    if (a.s.n_qtiles == 0) return;
+    const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
+    if constexpr (D <= 256) {
+      if (pre)
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T, PAD, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dq_pair_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
+    }
+    e = hipGetLastError();
+  };
+  if (fuse) {
+    run_dq(true);
+    if (e != hipSuccess) return (int)e;
+  } else if ((passes & kPassPre) && rows > 0) {
     hipLaunchKernelGGL((attn_bwd_pre_kernel<D, T>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
@@ -1483,15 +1536,7 @@ static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
     }
     if ((e = hipGetLastError()) != hipSuccess) return (int)e;
   }
-  if ((passes & kPassDq) && a.s.n_qtiles > 0) {
-    const dim3 grid(a.s.batch * a.s.hq * a.s.n_qtiles);
-    if constexpr (D <= 256) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((attn_bwd_dq_pair_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return (int)e;
-  }
+  if (!fuse && (passes & kPassDq)) run_dq(false);
   return (int)e;
 }
 

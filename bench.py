@@ -42,10 +42,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
 # source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
 TRAFFIC = {
-    ("dense_d128", "bwd_dkdv"): {"src_sha1": "27596cf22163", "bytes": 692874793},
-    ("dense_d128", "fwd"): {"src_sha1": "27596cf22163", "bytes": 859773610},
-    ("dense_d128", "bwd_dq"): {"src_sha1": "27596cf22163", "bytes": 854855376},
-    ("dense_d128", "bwd_pre"): {"src_sha1": "27596cf22163", "bytes": 159446840},
+    ("dense_d128", "bwd_dkdv"): {"src_sha1": "9dc7eb2f04f4", "bytes": 691958390},
+    ("dense_d128", "fwd"): {"src_sha1": "9dc7eb2f04f4", "bytes": 885035458},
+    ("dense_d128", "bwd_dq"): {"src_sha1": "9dc7eb2f04f4", "bytes": 925369449},
 }
 
 

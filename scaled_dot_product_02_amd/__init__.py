@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     attn_fwd,
     attn_fwd_workspace_bytes,
     attn_merge,
+    attn_mfma_probe,
     lib,
     library_path,
     make_problem,

@@ -19,7 +19,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess",
-            "attn_merge",
+            "attn_merge", "attn_mfma_probe",
             "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
             "attn_abi_version")
 MERGE_MAX_PARTS = 8
@@ -86,6 +86,9 @@ def lib():
             getattr(L, name).restype = ctypes.c_int
         L.attn_merge.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
         L.attn_merge.restype = ctypes.c_int
+        L.attn_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, vp, sz, vp, sz,
+                                      vp]
+        L.attn_mfma_probe.restype = ctypes.c_int
         L.attn_fwd_workspace_bytes.argtypes = [pp]
         L.attn_fwd_workspace_bytes.restype = sz
         L.attn_bwd_workspace_bytes.argtypes = [pp]
@@ -307,3 +310,17 @@ def attn_merge(o_parts, lse_parts, cu_seqlens_q=None, max_seqlen_q=None, out=Non
     if st != 0:
         _raise(st)
     return out, lse
+
+
+def attn_mfma_probe(blocks, iters, x=0.5, y=1.0 / 512, device="cuda:0", stream=None):
+    """Matrix-core rate probe (attn_mfma_probe): launches it on `stream` and returns (out, ticks), a
+    float32 [blocks * 256] checksum tensor and an int64 [blocks, 2] tensor of (shader-clock ticks,
+    100 MHz ticks) per workgroup, both on `device`. One call executes blocks * 4 * iters * 4 * 32768 FLOP."""
+    import torch
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    ticks = torch.empty((blocks, 2), dtype=torch.int64, device=device)
+    st = lib().attn_mfma_probe(int(blocks), int(iters), float(x), float(y), _ptr(out), out.numel() * 4, _ptr(ticks),
+                               ticks.numel() * 8, _stream(stream))
+    if st != 0:
+        _raise(st)
+    return out, ticks

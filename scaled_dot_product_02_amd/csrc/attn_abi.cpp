@@ -7,6 +7,7 @@
 // overlap before launching. Pull request 3527 ("cuDNN FROST attention backend for head_dim in
 // (256, 512], with context parallelism"), sections Notes for reviewers and Scope: unsupported
 // configurations are declined explicitly with a reason, never served by a different computation.
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
@@ -505,6 +506,34 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
     a.alse = lse_addr(p, in.packed);
     const int e = sdpa::launch_merge(p->dtype, sdpa::instance_head_dim(dv, dv), a, stream);
     if (e) return fail(ATTN_E_HIP, "merge launch: %s", hipGetErrorString((hipError_t)e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_INVALID, "internal error");
+  }
+}
+
+// Matrix-core rate probe (include/attn.h): a measurement aid, not part of the attention path.
+attn_status_t attn_mfma_probe(int32_t blocks, int32_t iters, float x, float y, float* out, size_t out_bytes,
+                              uint64_t* ticks, size_t ticks_bytes, void* stream) {
+  try {
+    if (blocks < 1 || blocks > ATTN_PROBE_MAX_BLOCKS)
+      return fail(ATTN_E_INVALID, "blocks %d is not in [1, %d]", blocks, ATTN_PROBE_MAX_BLOCKS);
+    if (iters < 1 || iters > ATTN_PROBE_MAX_ITERS)
+      return fail(ATTN_E_INVALID, "iters %d is not in [1, %d]", iters, ATTN_PROBE_MAX_ITERS);
+    if (!std::isfinite(x) || !std::isfinite(y)) return fail(ATTN_E_INVALID, "x and y must be finite");
+    if (!out || !ticks) return fail(ATTN_E_INVALID, "out or ticks is NULL");
+    if (!aligned(out, 4)) return fail(ATTN_E_ALIGN, "out is not 4-byte aligned");
+    if (!aligned(ticks, 8)) return fail(ATTN_E_ALIGN, "ticks is not 8-byte aligned");
+    if (out_bytes < (size_t)blocks * 256 * sizeof(float))
+      return fail(ATTN_E_WORKSPACE, "out holds %zu bytes, %zu needed", out_bytes, (size_t)blocks * 256 * sizeof(float));
+    if (ticks_bytes < (size_t)blocks * 2 * sizeof(uint64_t))
+      return fail(ATTN_E_WORKSPACE, "ticks holds %zu bytes, %zu needed", ticks_bytes,
+                  (size_t)blocks * 2 * sizeof(uint64_t));
+    const uintptr_t o0 = (uintptr_t)out, o1 = o0 + (size_t)blocks * 256 * sizeof(float);
+    const uintptr_t t0 = (uintptr_t)ticks, t1 = t0 + (size_t)blocks * 2 * sizeof(uint64_t);
+    if (o0 < t1 && t0 < o1) return fail(ATTN_E_OVERLAP, "out overlaps ticks");
+    const int e = sdpa::launch_mfma_probe(blocks, iters, x, y, out, (unsigned long long*)ticks, stream);
+    if (e) return fail(ATTN_E_HIP, "probe launch: %s", hipGetErrorString((hipError_t)e));
     return ATTN_OK;
   } catch (...) {
     return fail(ATTN_E_INVALID, "internal error");

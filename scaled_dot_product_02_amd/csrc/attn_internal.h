@@ -83,6 +83,9 @@ int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream);
 enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassDqPre = 8, kPassAll = 7 };
 int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream);
 int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
+// Matrix-core rate probe (attn_probe.hip): blocks x 256 threads, iters rounds of four MFMAs per wave.
+int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsigned long long* ticks,
+                      void* stream);
 int fwd_query_tile(int head_dim);
 int bwd_key_tile(int head_dim);
 int bwd_query_tile(int head_dim);

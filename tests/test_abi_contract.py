@@ -347,3 +347,25 @@ def test_extents_use_each_tensors_head_dim(L):
     k_addr = O + q_bytes + 4096          # past a D=64 O, inside a D=512 O
     assert k_addr < O + o_bytes_wide
     expect(L, fwd(L, p, k=k_addr), OVERLAP, "o overlaps an input")
+
+
+def test_mfma_probe_declines(L):
+    """The matrix-core probe validates its arguments before launching (no GPU needed for these)."""
+    out, ticks = 1 << 20, 1 << 24  # fake aligned device addresses, never dereferenced
+    nout, nticks = 4 * 256 * 4, 4 * 16
+
+    def call(blocks=4, iters=10, x=0.5, y=0.0, o=out, ob=nout, t=ticks, tb=nticks):
+        return L.attn_mfma_probe(blocks, iters, x, y, o, ob, t, tb, None)
+
+    cases = [
+        (dict(blocks=0), INVALID, "blocks"), (dict(blocks=65537), INVALID, "blocks"),
+        (dict(iters=0), INVALID, "iters"), (dict(iters=(1 << 24) + 1), INVALID, "iters"),
+        (dict(x=float("nan")), INVALID, "finite"), (dict(y=float("inf")), INVALID, "finite"),
+        (dict(o=None), INVALID, "NULL"), (dict(t=None), INVALID, "NULL"),
+        (dict(o=out + 2), ALIGN, "out"), (dict(t=ticks + 4), ALIGN, "ticks"),
+        (dict(ob=nout - 4), WORKSPACE, "out holds"), (dict(tb=nticks - 8), WORKSPACE, "ticks holds"),
+        (dict(t=out + 64), OVERLAP, "overlaps"),
+    ]
+    for kw, want, frag in cases:
+        assert call(**kw) == want, kw
+        assert frag in L.attn_last_error().decode(), (kw, L.attn_last_error())

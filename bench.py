@@ -17,13 +17,16 @@ per-step time is reported under
 step; the dQ pass's second S/dP recompute is not credited) over its compulsory HBM
 bytes: below the balance point 2.5 PFLOP/s / 8 TB/s it is HBM-bound and "achieved"
 is compulsory bytes per second against 8 TB/s, else MFMA-bound and "achieved" is
-algorithmic FLOP/s against 2.5 PFLOP/s ("kernel_roofline" lists all four).
+algorithmic FLOP/s against 2.5 PFLOP/s ("kernel_roofline" lists every kernel of the step).
 "cpu_baseline" times the float64 CPU oracle on a bounded sample of the same
 workload. The default run also reports, under "extra", the D=512 workload and
 attn_merge (two forward results combined, the ring step) on the dense D=128
 query side, the latter against the HBM peak, and the HBM-bound short-sequence
-workload (B128 S256 D128). Prints one JSON line on stdout;
-diagnostics go to stderr.
+workload (B128 S256 D128), also with the 256 MB memory-side cache overwritten
+before every step; "sustained_mfma" (the rate and engine clock of
+attn_mfma_probe, MFMAs from registers only) and "telemetry" (rocm-smi clocks,
+power and temperature before and after the timed steps) give context for the
+fractions of peak. Prints one JSON line on stdout; diagnostics go to stderr.
 """
 
 import argparse
@@ -164,13 +167,14 @@ def cpu_baseline(w, x, budget_s=15.0, max_units=16):
     cu_q = x["cu_seqlens_q"].numpy() if w.packed else None
     cu_k = x["cu_seqlens_kv"].numpy() if w.packed else None
     grp = w.hq // w.hkv
-    done, flops, t_total = [], 0.0, 0.0
+    done, flops, t_total, t_fwd = [], 0.0, 0.0, 0.0
     nseq = len(x["seqlens_q"])
     order = [(b, g) for b in range(nseq) for g in range(w.hkv)]
     for unit in order[:max_units]:
         b, g = unit
         t0 = time.perf_counter()
         sdpa_fwd(f64["q"], f64["k"], f64["v"], mask, w.scale, cu_q, cu_k, units=[unit], window_left=w.window_left)
+        t_fwd += time.perf_counter() - t0
         sdpa_bwd(f64["q"], f64["k"], f64["v"], f64["do"], mask, w.scale, cu_q, cu_k, units=[unit],
                  window_left=w.window_left)
         t_total += time.perf_counter() - t0
@@ -186,11 +190,15 @@ def cpu_baseline(w, x, budget_s=15.0, max_units=16):
     except Exception:
         cores = os.cpu_count()
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "fwd_s": round(t_fwd, 3), "bwd_s": round(t_total - t_fwd, 3),
             "sample": f"{len(done)} of {len(order)} (sequence, kv-head) units of {w.name} ({grp} q-heads each), "
                       f"forward+backward, numpy float64, {t_total:.1f} s; credited FLOPs as for the GPU value"}
 
 
-def run(w, steps, warmup, want_events=True):
+def run(w, steps, warmup, want_events=True, flush_mall=False):
+    """Time `steps` steps of workload w. With flush_mall, a 512 MiB buffer is overwritten before every
+    timed step (outside the per-kernel events), so no input is still in the 256 MB memory-side cache
+    when a step starts; ms_step then includes the fill and only the per-kernel times are meaningful."""
     import torch
     import scaled_dot_product_02_amd as sd
     from scaled_dot_product_02_amd.workloads import make_inputs
@@ -227,12 +235,15 @@ def run(w, steps, warmup, want_events=True):
             sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=(pas,), **kw)
         mark(1 + len(seq))
 
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush_mall else None
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)] if want_events else None
     t0 = time.perf_counter()
     for i in range(steps):
+        if scratch is not None:
+            scratch.zero_()
         step(evs[i] if evs else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -273,6 +284,22 @@ def mfma_probe_measure(blocks=512, iters=150000, reps=5):
     return {"what": "attn_mfma_probe: independent bf16 32x32x16 MFMA chains from registers, no memory traffic",
             "tflops": round(best, 1), "frac_of_published_peak": round(best / PEAK_TFLOPS, 4),
             "clock_ghz": round(clocks[rates.index(best)], 3), "blocks": blocks, "iters": iters, "reps": reps}
+
+
+def telemetry():
+    """Engine clock, power and temperature as rocm-smi reports them (read-only; a child process).
+    Returns the fields of the first card whose names mention a clock, power or temperature, or the
+    error text when rocm-smi is unavailable."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        cards = json.loads(r.stdout)
+        card = next(v for k, v in cards.items() if k.startswith("card"))
+        return {k: v for k, v in card.items() if re.search(r"sclk|mclk|power|temperature", k, re.I)}
+    except Exception as e:  # telemetry is context only: never fail the run for it
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
 
 
 def merge_measure(w, parts=2, steps=20, warmup=3):
@@ -347,7 +374,9 @@ def main():
         print(json.dumps({"merge": merge_measure(w, steps=args.steps, warmup=args.warmup)}), flush=True)
         return
     log(f"workload {w.name}: {w.note}")
+    tele_before = telemetry() if not args.no_extra else None
     r = run(w, args.steps, args.warmup)
+    tele_after = telemetry() if not args.no_extra else None
     d, pairs = w.d, r["pairs"]
     fp = flop_per_pair(w)
     f_fwd, f_bwd = fp["fwd"] * pairs, fp["bwd"] * pairs
@@ -369,7 +398,9 @@ def main():
                    "heads_q": w.hq, "heads_kv": w.hkv, "seq_q": w.sq or r["x"]["max_seqlen_q"],
                    "seq_kv": w.skv or r["x"]["max_seqlen_kv"], "head_dim": d, "head_dim_v": w.d_v,
                    "mask": w.mask,
-                   "layout": "thd" if w.packed else "bshd", "window_left": w.window_left, "allowed_pairs": pairs},
+                   "layout": "thd" if w.packed else "bshd", "window_left": w.window_left, "allowed_pairs": pairs,
+                   "seed": w.seed, **({"seqlens": list(map(int, r["x"]["seqlens_q"])), "total_q": int(r["nrows"])}
+                                      if w.packed else {})},
         "frac_of_peak": round(value / PEAK_TFLOPS, 4),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
                 "frac_of_peak": round(f_fwd / (fwd_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},
@@ -383,6 +414,7 @@ def main():
                             for n, e in kroof.items()},
     }
     if not args.no_extra:
+        out["telemetry"] = {"before": tele_before, "after": tele_after}
         out["sustained_mfma"] = mfma_probe_measure()
     if not args.no_extra and w.name == "dense_d128":
         w2 = WORKLOADS["dense_d512"]
@@ -401,6 +433,12 @@ def main():
             "ms_per_step": round(r3["ms_step"], 4), "kernel_ms": {n: round(t, 4) for n, t in r3["kern_ms"].items()},
             "kernel_roofline": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in e.items()}
                                 for n, e in kr3.items()}}
+        # the same HBM-bound workload with the memory-side cache overwritten before every step
+        r4 = run(w3, max(5, args.steps // 3), 3, flush_mall=True)
+        kr4 = kernel_roofline(w3, r4["x"], r4["nrows"], r4["pairs"], r4["kern_ms"])
+        out["extra"]["short_d128_mall_flushed"] = {
+            "kernel_ms": {n: round(t, 4) for n, t in r4["kern_ms"].items()},
+            "kernel_hbm_frac": {n: round(e["frac"], 4) for n, e in kr4.items()}}
     if not args.no_cpu_baseline:
         log("timing the float64 CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(w, r["x"])

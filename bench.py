@@ -45,9 +45,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
 # source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
 TRAFFIC = {
-    ("dense_d128", "bwd_dkdv"): {"src_sha1": "9dc7eb2f04f4", "bytes": 691958390},
-    ("dense_d128", "fwd"): {"src_sha1": "9dc7eb2f04f4", "bytes": 885035458},
-    ("dense_d128", "bwd_dq"): {"src_sha1": "9dc7eb2f04f4", "bytes": 925369449},
+    ("dense_d128", "bwd_dkdv"): {"src_sha1": "1277da02feaa", "bytes": 699784746},
+    ("dense_d128", "fwd"): {"src_sha1": "1277da02feaa", "bytes": 874385037},
+    ("dense_d128", "bwd_dq"): {"src_sha1": "1277da02feaa", "bytes": 921628898},
 }
 
 

@@ -841,16 +841,27 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
       sa[kb] = pack8<T>(dp[0][kb][0], dp[0][kb][1], dp[0][kb][2], dp[0][kb][3], dp[1][kb][0], dp[1][kb][1],
                         dp[1][kb][2], dp[1][kb][3]);
     }
+    // dO and Q fragments of column group dt + 1 are read before the products of group dt, so each
+    // group's LDS latency overlaps the previous group's MFMAs (two fragment sets in flight)
+    v8s dob = cat44(lds_read_tr_at(smem, tb + 2 * QTILE), lds_read_tr_at(smem, tb + 2 * QTILE + 32 * D));
+    v8s qbt = cat44(lds_read_tr_at(smem, tb), lds_read_tr_at(smem, tb + 32 * D));
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = tb ^ (32 * dt);
-      const v8s dob = cat44(lds_read_tr_at(smem, o1 + 2 * QTILE), lds_read_tr_at(smem, o1 + 2 * QTILE + 32 * D));
-      const v8s qbt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
+      v8s dob_n = dob, qbt_n = qbt;
+      if (dt + 1 < D / 16) {
+        const int o1 = tb ^ (32 * (dt + 1));
+        dob_n = cat44(lds_read_tr_at(smem, o1 + 2 * QTILE), lds_read_tr_at(smem, o1 + 2 * QTILE + 32 * D));
+        qbt_n = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         dv[kb][dt] = Elem<T>::mma16(pa[kb], Elem<T>::cast(dob), dv[kb][dt]);
         dk[kb][dt] = Elem<T>::mma16(sa[kb], Elem<T>::cast(qbt), dk[kb][dt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      dob = dob_n;
+      qbt = qbt_n;
     }
    }
   }

@@ -24,7 +24,8 @@ attn_merge (two forward results combined, the ring step) on the dense D=128
 query side, the latter against the HBM peak, and the HBM-bound short-sequence
 workload (B128 S256 D128), also with the 256 MB memory-side cache overwritten
 before every step; "sustained_mfma" (the rate and engine clock of
-attn_mfma_probe, MFMAs from registers only) and "telemetry" (rocm-smi clocks,
+attn_mfma_probe, MFMAs from registers only), "hbm_copy" (a plain 1 GiB device
+copy) and "telemetry" (rocm-smi clocks,
 power and temperature before and after the timed steps) give context for the
 fractions of peak. Prints one JSON line on stdout; diagnostics go to stderr.
 """
@@ -286,6 +287,28 @@ def mfma_probe_measure(blocks=512, iters=150000, reps=5):
             "clock_ghz": round(clocks[rates.index(best)], 3), "blocks": blocks, "iters": iters, "reps": reps}
 
 
+def copy_rate(nbytes=1 << 30, reps=5):
+    """Measured HBM ceiling as context for the HBM-bound kernels: a plain device-to-device copy of
+    `nbytes` (torch's copy kernel), timed with HIP events on the current stream; bytes moved = read +
+    write. Returns the best of `reps`."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * nbytes / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del src, dst
+    return {"what": "device copy of 1 GiB (read + write counted)", "GB/s": round(best, 1),
+            "frac_of_published_peak": round(best / PEAK_HBM_GBS, 4)}
+
+
 def telemetry():
     """Engine clock, power and temperature as rocm-smi reports them (read-only; a child process).
     Returns the fields of the first card whose names mention a clock, power or temperature, or the
@@ -416,6 +439,7 @@ def main():
     if not args.no_extra:
         out["telemetry"] = {"before": tele_before, "after": tele_after}
         out["sustained_mfma"] = mfma_probe_measure()
+        out["hbm_copy"] = copy_rate()
     if not args.no_extra and w.name == "dense_d128":
         w2 = WORKLOADS["dense_d512"]
         r2 = run(w2, max(3, args.steps // 6), 2)

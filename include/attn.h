@@ -191,9 +191,9 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
                          const float* const* lse_parts, void* o, float* lse, void* stream);
 
 /* Matrix-core rate probe. A measurement aid beside the attention entry points, not part of the
- * attention computation: it gives the fraction-of-peak figures of the MFMA kernels (forward, dK/dV and
- * dQ passes, whose FLOP counts follow the attention definition in the pages' Scope and Approach
- * sections) a ceiling measured on the device next to the published one.
+ * attention computation (no page defines it): it gives the fraction-of-peak figures of the MFMA
+ * kernels (forward, dK/dV and dQ passes over the attention of pull request 3527, sections Scope and
+ * Approach) a ceiling measured on the device next to the published one.
  * Launches `blocks` workgroups of 256 threads on `stream`; every wave runs `iters` rounds of four
  * independent 32x32x16 bf16 MFMAs (32768 FLOP each) on register operands, with no memory traffic in
  * the loop, so one call executes blocks * 4 * iters * 4 * 32768 FLOP. Lane l of every wave uses the

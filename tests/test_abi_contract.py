@@ -369,3 +369,22 @@ def test_mfma_probe_declines(L):
     for kw, want, frag in cases:
         assert call(**kw) == want, kw
         assert frag in L.attn_last_error().decode(), (kw, L.attn_last_error())
+
+
+@pytest.mark.parametrize("entry", sorted(set(B.BWD_PASSES.values())))
+def test_every_backward_entry_point_validates(L, entry):
+    """Each backward entry point (attn_bwd and the single passes, the fused dQ + preprocess pass
+    included) runs the same host checks before any launch."""
+    fn = getattr(L, entry)
+
+    def call(p, ws_bytes=1 << 30, dq=DQ):
+        return fn(ctypes.byref(p), Q, K, V, O, DO, LSE, dq, DK, DV, WS, ws_bytes, None)
+
+    bad = dense_problem()
+    bad.head_dim = 100
+    expect(L, call(bad), UNSUPPORTED, "head_dim 100")
+    p = dense_problem()
+    need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    expect(L, call(p, ws_bytes=need - 256), WORKSPACE, "workspace")
+    expect(L, call(p, dq=DQ + 2), ALIGN, "dq")
+    expect(L, call(p, dq=DK), OVERLAP, "overlap")

@@ -46,9 +46,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
 # source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
 TRAFFIC = {
-    ("dense_d128", "bwd_dkdv"): {"src_sha1": "1277da02feaa", "bytes": 699784746},
-    ("dense_d128", "fwd"): {"src_sha1": "1277da02feaa", "bytes": 874385037},
-    ("dense_d128", "bwd_dq"): {"src_sha1": "1277da02feaa", "bytes": 921628898},
+    ("dense_d128", "bwd_dkdv"): {"src_sha1": "0c7c86e2dde8", "bytes": 699309987},
+    ("dense_d128", "fwd"): {"src_sha1": "0c7c86e2dde8", "bytes": 881545096},
+    ("dense_d128", "bwd_dq"): {"src_sha1": "0c7c86e2dde8", "bytes": 907839638},
 }
 
 

@@ -1192,13 +1192,25 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     v4f sv[2];  // role 0: S then P; role 1: dP then dS
     if (active) {
       const us* src = role == 0 ? qs : dos;
+      // the two 16-row blocks alternate (two independent accumulator chains) and the Q / dO fragments
+      // are read RA products ahead: the two waves of a SIMD move in step here and cannot hide each
+      // other's LDS latency
+      constexpr int NT = 2 * (D / 32), RA = 4;
+      v8s rb[RA];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        sv[qb] = v4f{};
+      for (int i = 0; i < RA; ++i) rb[i] = lds_read16(src, rrow + 16 * (i & 1) * D + ((32 * (i >> 1)) ^ rx));
+      sv[0] = v4f{};
+      sv[1] = v4f{};
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-          sv[qb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, rrow + 16 * qb * D + ((32 * kk) ^ rx))),
-                                  Elem<T>::cast(kvf[kk]), sv[qb]);
+      for (int t = 0; t < NT; ++t) {
+        const v8s x = rb[t % RA];
+        __builtin_amdgcn_sched_barrier(0);
+        sv[t & 1] = Elem<T>::mma16(Elem<T>::cast(x), Elem<T>::cast(kvf[t >> 1]), sv[t & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + RA < NT) {
+          const int u = t + RA;
+          rb[t % RA] = lds_read16(src, rrow + 16 * (u & 1) * D + ((32 * (u >> 1)) ^ rx));
+        }
       }
       if (role == 0) {
 #pragma unroll

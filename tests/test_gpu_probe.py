@@ -21,3 +21,6 @@ def test_probe_checksum_and_ticks(blocks, iters):
     if iters >= 1000:  # long enough for the 100 MHz reference counter to advance
         t = ticks.cpu()
         assert (t > 0).all(), t
+        # shader-clock ticks per 100 MHz tick: the engine clock, which lies between idle and boost
+        ghz = 0.1 * t[:, 0].double() / t[:, 1].double()
+        assert ((ghz > 0.5) & (ghz < 3.0)).all(), ghz

@@ -19,11 +19,15 @@ bytes: below the balance point 2.5 PFLOP/s / 8 TB/s it is HBM-bound and "achieve
 is compulsory bytes per second against 8 TB/s, else MFMA-bound and "achieved" is
 algorithmic FLOP/s against 2.5 PFLOP/s ("kernel_roofline" lists every kernel of the step).
 "cpu_baseline" times the float64 CPU oracle on a bounded sample of the same
-workload. The default run also reports, under "extra", the D=512 workload and
-attn_merge (two forward results combined, the ring step) on the dense D=128
-query side, the latter against the HBM peak, and the HBM-bound short-sequence
-workload (B128 S256 D128), also with the 256 MB memory-side cache overwritten
-before every step; "sustained_mfma" (the rate and engine clock of
+workload. The default run also times, under "cases", every other named case
+(tiny B1 H2 S128 D64 fp16; the packed GQA batch thd_d128; dense_d512; the two
+single-rank context-parallel shares at D=256 and D=512): forward, backward and
+combined ms, TFLOP/s and fraction of peak, compulsory-byte GB/s, per-kernel
+times, and the float64 oracle timed on a bounded slice of the same case. Under
+"extra" it reports attn_merge (two forward results combined, the ring step) on
+the dense D=128 query side against the HBM peak, and the HBM-bound
+short-sequence workload (B128 S256 D128), also with the 256 MB memory-side
+cache overwritten before every step; "sustained_mfma" (the rate and engine clock of
 attn_mfma_probe, MFMAs from registers only), "hbm_copy" (a plain 1 GiB device
 copy) and "telemetry" (rocm-smi clocks,
 power and temperature before and after the timed steps) give context for the
@@ -196,6 +200,42 @@ def cpu_baseline(w, x, budget_s=15.0, max_units=16):
                       f"forward+backward, numpy float64, {t_total:.1f} s; credited FLOPs as for the GPU value"}
 
 
+def oracle_sample(w, x, rows=512):
+    """The float64 oracle timed beside the GPU on a bounded slice of the workload: the last `rows` query rows
+    of the last sequence's last q-head against all of that sequence's keys. Under a causal mask those rows are
+    the bottom-right causal problem of themselves against every key (the slice keeps every allowed pair of the
+    rows it holds), so the seconds per allowed pair are the oracle's own. Returns fwd/bwd seconds and rates."""
+    import numpy as np
+    from oracle import MASK_CAUSAL_BR, MASK_NONE, head_backward, head_forward
+    b = len(x["seqlens_q"]) - 1
+    h = w.hq - 1
+    g = h // (w.hq // w.hkv)
+    lq, lk = x["seqlens_q"][b], x["seqlens_kv"][b]
+    r = min(rows, lq)
+    if w.packed:
+        q0, k0 = int(x["cu_seqlens_q"][b]), int(x["cu_seqlens_kv"][b])
+        qs, ks = slice(q0 + lq - r, q0 + lq), slice(k0, k0 + lk)
+        pick_q = lambda t: t[qs, h]  # noqa: E731
+        pick_k = lambda t: t[ks, g]  # noqa: E731
+    else:
+        pick_q = lambda t: t[b, lq - r:, h]  # noqa: E731
+        pick_k = lambda t: t[b, :, g]  # noqa: E731
+    f = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    qh, doh, kh, vh = f(pick_q(x["q"])), f(pick_q(x["do"])), f(pick_k(x["k"])), f(pick_k(x["v"]))
+    mask = MASK_NONE if w.mask == "none" else MASK_CAUSAL_BR
+    t0 = time.perf_counter()
+    head_forward(qh, kh, vh, w.scale, mask, w.window_left)
+    t1 = time.perf_counter()
+    head_backward(qh, kh, vh, doh, w.scale, mask, w.window_left)
+    t2 = time.perf_counter()
+    pairs = allowed_pairs([r], [lk], "none" if w.mask == "none" else "causal_br", w.window_left)
+    fp = flop_per_pair(w)
+    return {"kind": "oracle", "sample": f"last {r} query rows of sequence {b}, q-head {h}, against its {lk} keys",
+            "pairs": pairs, "fwd_s": round(t1 - t0, 4), "bwd_s": round(t2 - t1, 4),
+            "fwd_tflops": round(fp["fwd"] * pairs / (t1 - t0) / 1e12, 5),
+            "bwd_tflops": round(fp["bwd"] * pairs / (t2 - t1) / 1e12, 5)}
+
+
 def run(w, steps, warmup, want_events=True, flush_mall=False):
     """Time `steps` steps of workload w. With flush_mall, a 512 MiB buffer is overwritten before every
     timed step (outside the per-kernel events), so no input is still in the 256 MB memory-side cache
@@ -357,6 +397,44 @@ def merge_measure(w, parts=2, steps=20, warmup=3):
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def case_measure(w, steps, warmup, oracle_rows=512):
+    """One named case: forward, backward and combined time and TFLOP/s (algorithmic FLOPs over the exact
+    allowed pairs) with the per-kernel launch times, the compulsory-byte rates (GB/s against the HBM peak;
+    the measure that matters for latency-bound tiny cases) and the oracle timed on a bounded slice."""
+    r = run(w, steps, warmup)
+    fp = flop_per_pair(w)
+    km = r["kern_ms"]
+    fwd_ms = km["fwd"]
+    bwd_ms = sum(t for n, t in km.items() if n != "fwd")
+    pairs = r["pairs"]
+    f_fwd, f_bwd = fp["fwd"] * pairs, fp["bwd"] * pairs
+    nb = compulsory_bytes(w, r["x"], r["nrows"])
+    bwd_bytes = sum(nb[n] for n in km if n != "fwd")
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12  # noqa: E731
+    out = {"config": w.note, "steps": steps, "warmup": warmup, "allowed_pairs": pairs,
+           "ms_per_step": round(r["ms_step"], 4),
+           "fwd": {"ms": round(fwd_ms, 4), "us": round(fwd_ms * 1e3, 2), "tflops": round(tf(f_fwd, fwd_ms), 2),
+                   "frac_of_peak": round(tf(f_fwd, fwd_ms) / PEAK_TFLOPS, 4),
+                   "GB/s": round(nb["fwd"] / (fwd_ms * 1e-3) / 1e9, 1)},
+           "bwd": {"ms": round(bwd_ms, 4), "us": round(bwd_ms * 1e3, 2), "tflops": round(tf(f_bwd, bwd_ms), 2),
+                   "frac_of_peak": round(tf(f_bwd, bwd_ms) / PEAK_TFLOPS, 4),
+                   "GB/s": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1)},
+           "fwd_bwd": {"tflops": round(tf(f_fwd + f_bwd, fwd_ms + bwd_ms), 2),
+                       "frac_of_peak": round(tf(f_fwd + f_bwd, fwd_ms + bwd_ms) / PEAK_TFLOPS, 4)},
+           "kernel_ms": {n: round(t, 4) for n, t in km.items()},
+           "kernel_ms_min": {n: round(t, 4) for n, t in r["kern_min"].items()}}
+    if w.packed:
+        out["seqlens"] = list(map(int, r["x"]["seqlens_q"]))
+    if oracle_rows:
+        out["oracle"] = oracle_sample(w, r["x"], oracle_rows)
+    return out
+
+
+# The named cases timed in every default run besides the headline (dense_d128): the tiny case, the packed
+# GQA batch, the D=512 layer and the two single-rank context-parallel shares.
+CASES = ("tiny", "thd_d128", "dense_d512", "cp_share_d256", "cp_share_d512")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,7 +442,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the informational D=512, merge and short-sequence lines")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other named cases and the informational merge and short-sequence lines")
     ap.add_argument("--merge-only", action="store_true",
                     help="only time attn_merge of two forward results (dense_d128 query side) and print its line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -441,15 +520,12 @@ def main():
         out["sustained_mfma"] = mfma_probe_measure()
         out["hbm_copy"] = copy_rate()
     if not args.no_extra and w.name == "dense_d128":
-        w2 = WORKLOADS["dense_d512"]
-        r2 = run(w2, max(3, args.steps // 6), 2)
-        fp2 = flop_per_pair(w2)
-        f2 = (fp2["fwd"] + fp2["bwd"]) * r2["pairs"]
-        km2 = r2["kern_ms"]
-        out["extra"] = {"dense_d512": {"tflops": round(f2 / (r2["ms_step"] * 1e-3) / 1e12, 2),
-                                       "ms_per_step": round(r2["ms_step"], 4),
-                                       "kernel_ms": {n: round(t, 4) for n, t in km2.items()}},
-                        "merge": merge_measure(w)}
+        out["cases"] = {}
+        for name in CASES:
+            wc = WORKLOADS[name]
+            log(f"case {name}: {wc.note}")
+            out["cases"][name] = case_measure(wc, max(5, args.steps // 2), 3)
+        out["extra"] = {"merge": merge_measure(w)}
         w3 = WORKLOADS["short_d128"]
         r3 = run(w3, max(5, args.steps // 3), 3)
         kr3 = kernel_roofline(w3, r3["x"], r3["nrows"], r3["pairs"], r3["kern_ms"])

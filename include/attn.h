@@ -120,43 +120,57 @@ typedef struct attn_problem {
   int32_t head_dim_v;  /* D_v: head dim of V, O (multiple of 8 in [8, 512]); 0 = head_dim (ABI 3) */
 } attn_problem_t;
 
-/* Workspace. Its first 256 bytes are a header whose int32 at offset 0 is the device error word:
- * 0 after a call whose packed sequence lengths were valid, otherwise a nonzero code (bit 0: first
- * offset not zero; bit 1: decreasing offsets; bit 2: last offset differs from total_q/total_kv;
- * bit 3: a length exceeds max_seqlen; bit 4: queries without keys). The word is written by every
- * call (no pre-clearing needed). Dense forward calls need no workspace (0 bytes; ws may be NULL).
+/* Workspace (pull request 3705, section Execution and supported scope: the caller binds the workspace
+ * on every call; pull request 3527, section Known limitations: the backward workspace there grows
+ * super-linearly, here it is linear in tokens). Its first 256 bytes are a header whose int32 at
+ * offset 0 is the device error word: every call on a packed batch (attn_fwd, attn_bwd and each
+ * backward pass on its own) first rewrites it from this call's cu_seqlens, 0 when they are valid,
+ * otherwise a nonzero code (bit 0: first offset not zero; bit 1: decreasing offsets; bit 2: last
+ * offset differs from total_q/total_kv; bit 3: a length exceeds max_seqlen; bit 4: queries without
+ * keys), so no pre-clearing is needed and a stale word from another call is never trusted. Dense
+ * calls neither read nor write it. Dense forward calls need no workspace (0 bytes; ws may be NULL).
  * The backward workspace is linear in the number of query tokens: header + two fp32 [Hq x tokens]
  * arrays (row sums D = rowsum(dO * O), and LSE in log2 units). Sizes are multiples of 256. */
 size_t attn_fwd_workspace_bytes(const attn_problem_t* p);
 size_t attn_bwd_workspace_bytes(const attn_problem_t* p);
 
-/* Forward: O = softmax(mask(scale * Q K^T)) V and LSE = log(sum_j exp(S_ij)) (natural log, fp32).
+/* Forward (pull request 3527, sections Approach and Scope: fused attention with the mask vocabulary
+ * above; pull request 3705, section Execution and supported scope: the forward returns fp32 Stats in
+ * natural log, token-major for packed batches):
+ * O = softmax(mask(scale * Q K^T)) V and LSE = log(sum_j exp(S_ij)) (natural log, fp32).
  * q, k, v: device inputs in p->dtype; o: device output (O's strides); lse: device fp32 output;
  * ws: device workspace of ws_bytes >= attn_fwd_workspace_bytes(p), 256-byte aligned;
  * stream: the hipStream_t to launch on (NULL = the default stream). Pointers and strides must
- * be 16-byte aligned (strides multiples of 8 elements); lse 4-byte aligned. */
+ * be 16-byte aligned (strides multiples of 8 elements); lse 4-byte aligned. Every element of o and
+ * lse is written (rows with no allowed key: O = 0, LSE = -inf). */
 attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, const void* v, void* o,
                        float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward from the saved LSE: given dO, returns dQ, dK, dV of the forward above.
+/* Backward (pull request 3527, sections Approach and Scope: the backward of the same fused attention,
+ * producing dQ, dK, dV; pull request 3705, section Execution and supported scope: the backward
+ * consumes the forward's natural-log Stats): given dO, returns dQ, dK, dV of the forward above,
+ * recomputing P from the saved LSE.
  * o and lse must be the forward's outputs for the same q, k, v (O is used for the row sums
  * D = rowsum(dO * O)); d_o uses O's strides. dK and dV of kv-head g sum over the q-heads of
- * g's group. Every element of dq, dk, dv is written (keys that no query sees get zeros). */
+ * g's group. Every element of dq, dk, dv is written (keys that no query sees get zeros). The result
+ * is bitwise deterministic: every output element has one writer and a fixed summation order. */
 attn_status_t attn_bwd(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
                        const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* ws,
                        size_t ws_bytes, void* stream);
 
 /* The passes of the backward as separate calls with attn_bwd's arguments (each validates the whole
- * argument list the same way). The backward is defined by the method as these steps: preprocess
- * D = rowsum(dO * O) (and LSE in log2 units, +inf for rows with no key) into the workspace, writing
- * the error word for packed batches; the dK/dV pass, which writes dk and dv; the dQ pass, which
- * writes dq. dkdv and dq read what preprocess left in the same workspace for the same problem and
- * inputs, so they must follow it on the same stream (or after an event); they are independent of
- * each other. attn_bwd_dq_preprocess is the dQ pass with the preprocess folded in (it writes the
- * workspace's D and LSE rows for attn_bwd_dkdv, which must follow it): attn_bwd runs
- * attn_bwd_dq_preprocess then attn_bwd_dkdv for head dims up to 256, and the three passes in the
- * order preprocess, dkdv, dq for wider heads. Every split computes the same quantities (up to the
- * summation order of D). Splitting them lets a caller time or overlap the passes. */
+ * argument list the same way). The method's backward consists of these steps (pull request 3527,
+ * section Approach; pull request 3705, section Execution and supported scope, for the Stats it
+ * reads): preprocess D = rowsum(dO * O) (and LSE in log2 units, +inf for rows with no key) into the
+ * workspace; the dK/dV pass, which writes dk and dv; the dQ pass, which writes dq. dkdv and dq read
+ * what preprocess left in the same workspace for the same problem and inputs, so they must follow it
+ * on the same stream (or after an event); they are independent of each other. Each call on a packed
+ * batch rewrites the error word from its own cu_seqlens first. attn_bwd_dq_preprocess is the dQ pass
+ * with the preprocess folded in (it writes the workspace's D and LSE rows for attn_bwd_dkdv, which
+ * must follow it): attn_bwd runs attn_bwd_dq_preprocess then attn_bwd_dkdv for head dims up to 256,
+ * and the three passes in the order preprocess, dkdv, dq for wider heads. Every split computes the
+ * same quantities (up to the summation order of D). Splitting them lets a caller time or overlap the
+ * passes. */
 attn_status_t attn_bwd_preprocess(const attn_problem_t* p, const void* q, const void* k, const void* v,
                                   const void* o, const void* d_o, const float* lse, void* dq, void* dk, void* dv,
                                   void* ws, size_t ws_bytes, void* stream);
@@ -189,29 +203,6 @@ attn_status_t attn_bwd_dq_preprocess(const attn_problem_t* p, const void* q, con
 #define ATTN_MERGE_MAX_PARTS 8
 attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* const* o_parts,
                          const float* const* lse_parts, void* o, float* lse, void* stream);
-
-/* Matrix-core rate probe. A measurement aid beside the attention entry points, not part of the
- * attention computation (no page defines it): it gives the fraction-of-peak figures of the MFMA
- * kernels (forward, dK/dV and dQ passes over the attention of pull request 3527, sections Scope and
- * Approach) a ceiling measured on the device next to the published one.
- * Launches `blocks` workgroups of 256 threads on `stream`; every wave runs `iters` rounds of four
- * independent 32x32x16 bf16 MFMAs (32768 FLOP each) on register operands, with no memory traffic in
- * the loop, so one call executes blocks * 4 * iters * 4 * 32768 FLOP. Lane l of every wave uses the
- * operands A[t] = bf16(x + y * (l + 8t)) and B[t] = bf16(x - y * (l + 8t)), t = 0..7.
- *   out    device float[blocks * 256] (out_bytes at least that): thread i of workgroup w writes the sum
- *          of its 64 accumulator values to out[256 w + i]; with y = 0 that sum is
- *          1024 * bf16(x)^2 * iters (a check that every MFMA ran).
- *   ticks  device uint64[2 * blocks] (ticks_bytes at least that): ticks[2w] = shader-clock ticks and
- *          ticks[2w + 1] = 100 MHz reference ticks that wave 0 of workgroup w spent in the loop, so
- *          100 MHz * ticks[2w] / ticks[2w + 1] is the engine clock it ran at.
- * blocks in [1, ATTN_PROBE_MAX_BLOCKS], iters in [1, ATTN_PROBE_MAX_ITERS], x and y finite, out 4-byte
- * and ticks 8-byte aligned, the two not overlapping; otherwise nothing is launched and the status says
- * why (ATTN_E_INVALID / ATTN_E_ALIGN / ATTN_E_WORKSPACE / ATTN_E_OVERLAP). Asynchronous on `stream`;
- * the caller owns both buffers. */
-#define ATTN_PROBE_MAX_BLOCKS 65536
-#define ATTN_PROBE_MAX_ITERS (1 << 24)
-attn_status_t attn_mfma_probe(int32_t blocks, int32_t iters, float x, float y, float* out, size_t out_bytes,
-                              uint64_t* ticks, size_t ticks_bytes, void* stream);
 
 const char* attn_status_str(attn_status_t s); /* static string naming the status code          */
 const char* attn_last_error(void);            /* thread-local reason for this thread's last error */

@@ -129,6 +129,75 @@ def _check_device(*ts):
             raise ValueError("the head dimension must be contiguous (stride 1)")
 
 
+def _shape_of(t):
+    return tuple(t.shape)
+
+
+def _check_tensors(q, k, v, packed, cu_seqlens_q=None, cu_seqlens_kv=None, o=None, do=None, lse=None, dq=None,
+                   dk=None, dv=None):
+    """Every tensor must agree with q before any pointer reaches the library, which sizes every extent from
+    the problem it builds out of q, k and v: one 16-bit dtype (bf16 or fp16) for Q, K, V, O, dO, dQ, dK, dV;
+    the documented shapes (dense Q [B,Sq,Hq,Dqk], K [B,Skv,Hkv,Dqk], V [B,Skv,Hkv,Dv], O and dO
+    [B,Sq,Hq,Dv]; packed Q [Tq,Hq,Dqk], K [Tkv,Hkv,Dqk], V [Tkv,Hkv,Dv], O and dO [Tq,Hq,Dv]); dQ, dK, dV the
+    shapes of Q, K, V; LSE contiguous float32 [B,Hq,Sq] or [Tq,Hq]; cu_seqlens contiguous 1-D int32 of one
+    length; all on one device. Raises ValueError naming the first mismatch."""
+    import torch
+    nd = 3 if packed else 4
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != nd:
+            raise ValueError(f"{n} must be {'[T,H,D]' if packed else '[B,S,H,D]'}; got shape {_shape_of(t)}")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"q must be bfloat16 or float16; got {q.dtype}")
+    if packed:
+        tq, hq, dqk = q.shape
+        tk, hkv, dk_ = k.shape
+        if dk_ != dqk:
+            raise ValueError(f"k head dim {dk_} differs from q's {dqk}")
+        if tuple(v.shape[:2]) != (tk, hkv):
+            raise ValueError(f"v shape {_shape_of(v)} does not match k's tokens and heads {(tk, hkv)}")
+        dvh = v.shape[2]
+        o_shape, lse_shape = (tq, hq, dvh), (tq, hq)
+    else:
+        b, sq, hq, dqk = q.shape
+        if k.shape[0] != b or k.shape[3] != dqk:
+            raise ValueError(f"k shape {_shape_of(k)} does not match q's batch {b} and head dim {dqk}")
+        _, skv, hkv, _ = k.shape
+        if tuple(v.shape[:3]) != (b, skv, hkv):
+            raise ValueError(f"v shape {_shape_of(v)} does not match k's {(b, skv, hkv)}")
+        dvh = v.shape[3]
+        o_shape, lse_shape = (b, sq, hq, dvh), (b, hq, sq)
+    expect = {"k": (k, None), "v": (v, None), "o": (o, o_shape), "do": (do, o_shape), "dq": (dq, tuple(q.shape)),
+              "dk": (dk, tuple(k.shape)), "dv": (dv, tuple(v.shape))}
+    for n, (t, shape) in expect.items():
+        if t is None:
+            continue
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} has dtype {t.dtype}; every attention tensor must have q's dtype {q.dtype}")
+        if shape is not None and _shape_of(t) != shape:
+            raise ValueError(f"{n} must have shape {shape}; got {_shape_of(t)}")
+    if lse is not None:
+        if lse.dtype != torch.float32:
+            raise ValueError(f"lse must be float32; got {lse.dtype}")
+        if _shape_of(lse) != lse_shape:
+            raise ValueError(f"lse must have shape {lse_shape}; got {_shape_of(lse)}")
+        if not lse.is_contiguous():
+            raise ValueError("lse must be contiguous")
+    if packed:
+        for n, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+            if c is None:
+                raise ValueError("packed batches need both cu_seqlens_q and cu_seqlens_kv")
+            if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+                raise ValueError(f"{n} must be a contiguous 1-D int32 tensor")
+        if cu_seqlens_q.numel() != cu_seqlens_kv.numel() or cu_seqlens_q.numel() < 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_kv must both hold batch + 1 >= 1 entries")
+    elif cu_seqlens_kv is not None:
+        raise ValueError("cu_seqlens_kv given without cu_seqlens_q")
+    ts = [t for t in (q, k, v, o, do, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv) if t is not None]
+    if any(t.device != q.device for t in ts):
+        raise ValueError("all attention tensors must be on one device")
+    _check_device(*ts)
+
+
 def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
                  window_left=-1):
     packed = cu_seqlens_q is not None
@@ -199,8 +268,8 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
     LSE is fp32 [B,Hq,Sq] (dense) or [Tq,Hq] (packed).
     """
     import torch
-    _check_device(q, k, v, out, cu_seqlens_q, cu_seqlens_kv)
     packed = cu_seqlens_q is not None
+    _check_tensors(q, k, v, packed, cu_seqlens_q, cu_seqlens_kv, o=out, lse=lse)
     if out is None:
         out = torch.empty(q.shape[:-1] + v.shape[-1:], dtype=q.dtype, device=q.device)
     if lse is None:
@@ -230,7 +299,8 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
     attn_bwd runs for head dims up to 256).
     """
     import torch
-    _check_device(q, k, v, o, do, lse, dq, dk, dv, cu_seqlens_q, cu_seqlens_kv)
+    _check_tensors(q, k, v, cu_seqlens_q is not None, cu_seqlens_q, cu_seqlens_kv, o=o, do=do, lse=lse, dq=dq,
+                   dk=dk, dv=dv)
     if do.stride() != o.stride():
         raise ValueError("dO must have the same strides as O")
     if dq is None:
@@ -291,11 +361,27 @@ def attn_merge(o_parts, lse_parts, cu_seqlens_q=None, max_seqlen_q=None, out=Non
     o_parts, lse_parts = list(o_parts), list(lse_parts)
     if not o_parts or len(o_parts) != len(lse_parts):
         raise ValueError("o_parts and lse_parts must be non-empty and of equal length")
-    _check_device(*o_parts, *lse_parts, out, lse, cu_seqlens_q)
     ref = o_parts[0]
+    packed = cu_seqlens_q is not None
+    if ref.dim() != (3 if packed else 4):
+        raise ValueError(f"o_parts must be {'[Tq,Hq,D]' if packed else '[B,Sq,Hq,D]'}; got shape {tuple(ref.shape)}")
+    if ref.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"o_parts must be bfloat16 or float16; got {ref.dtype}")
     for x in o_parts:
         if x.shape != ref.shape or x.stride() != ref.stride() or x.dtype != ref.dtype:
             raise ValueError("all parts of O must share shape, strides and dtype")
+    lse_shape = (ref.shape[0], ref.shape[1]) if packed else (ref.shape[0], ref.shape[2], ref.shape[1])
+    for x in lse_parts + ([lse] if lse is not None else []):
+        if x.dtype != torch.float32 or tuple(x.shape) != lse_shape or not x.is_contiguous():
+            raise ValueError(f"every LSE must be contiguous float32 of shape {lse_shape}")
+    if out is not None and (out.shape != ref.shape or out.dtype != ref.dtype):
+        raise ValueError("out must have the parts' shape and dtype")
+    if packed and (cu_seqlens_q.dtype != torch.int32 or cu_seqlens_q.dim() != 1):
+        raise ValueError("cu_seqlens_q must be a 1-D int32 tensor")
+    ts = [t for t in (*o_parts, *lse_parts, out, lse, cu_seqlens_q) if t is not None]
+    if any(t.device != ref.device for t in ts):
+        raise ValueError("all tensors must be on one device")
+    _check_device(*ts)
     if out is None:
         out = torch.empty_like(ref)
     if out.stride() != ref.stride():

@@ -17,6 +17,7 @@
 #include <string>
 
 #include "../../include/attn.h"
+#include "../../include/attn_probe.h"
 #include "attn_internal.h"
 
 namespace {
@@ -293,11 +294,14 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
     if (overlaps(eo, el)) return fail(ATTN_E_OVERLAP, "o overlaps lse");
     if (overlaps(ew, eo) || overlaps(ew, el) || overlaps(ew, eq) || overlaps(ew, ek) || overlaps(ew, ev))
       return fail(ATTN_E_OVERLAP, "workspace overlaps a tensor");
-    if (p->batch == 0 || in.nq == 0) return ATTN_OK;  // no query row: nothing to write
-
     sdpa::FwdArgs a{};
     const int inst = sdpa::instance_head_dim(dqk, dv);
     a.s = make_shape(p, in, ws, sdpa::fwd_query_tile(inst));
+    if (in.packed) {  // every packed call rewrites the error word from its own offsets
+      const int e = sdpa::launch_validate_cu(a.s, stream);
+      if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    if (p->batch == 0 || in.nq == 0) return ATTN_OK;  // no query row: nothing to write
     a.q = q;
     a.k = k;
     a.v = v;
@@ -308,10 +312,6 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
     a.av = addr(p->v_stride, in.packed);
     a.ao = addr(p->o_stride, in.packed);
     a.alse = lse_addr(p, in.packed);
-    if (in.packed) {
-      const int e = sdpa::launch_validate_cu(a.s, stream);
-      if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
-    }
     if (a.s.n_qtiles == 0) return ATTN_OK;
     const int e = sdpa::launch_fwd(p->dtype, inst, a, stream);
     if (e) return fail(ATTN_E_HIP, "forward launch: %s", hipGetErrorString((hipError_t)e));
@@ -362,11 +362,15 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     }
     for (int i = 0; i < 6; ++i)
       if (overlaps(ew, *ins[i])) return fail(ATTN_E_OVERLAP, "workspace overlaps an input");
-    if (p->batch == 0 || (in.nq == 0 && in.nkv == 0)) return ATTN_OK;
-
     sdpa::BwdArgs a{};
     const int inst = sdpa::instance_head_dim(dqk, dvw);
     a.s = make_shape(p, in, ws, sdpa::bwd_query_tile(inst));
+    if (in.packed) {  // every packed call (each pass on its own too) rewrites the error word first
+      const int e = sdpa::launch_validate_cu(a.s, stream);
+      if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    if (p->batch == 0 || (in.nq == 0 && in.nkv == 0)) return ATTN_OK;
+
     a.q = q;
     a.k = k;
     a.v = v;
@@ -386,10 +390,6 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     a.alse = lse_addr(p, in.packed);
     const int kt = sdpa::bwd_key_tile(inst);
     a.n_kvtiles = (p->max_seqlen_kv + kt - 1) / kt;
-    if (in.packed && (passes & (sdpa::kPassPre | sdpa::kPassDqPre))) {
-      const int e = sdpa::launch_validate_cu(a.s, stream);
-      if (e) return fail(ATTN_E_HIP, "validate launch: %s", hipGetErrorString((hipError_t)e));
-    }
     const int e = sdpa::launch_bwd(p->dtype, inst, a, passes, stream);
     if (e) return fail(ATTN_E_HIP, "backward launch: %s", hipGetErrorString((hipError_t)e));
     return ATTN_OK;
@@ -512,7 +512,7 @@ attn_status_t attn_merge(const attn_problem_t* p, int32_t n_parts, const void* c
   }
 }
 
-// Matrix-core rate probe (include/attn.h): a measurement aid, not part of the attention path.
+// Matrix-core rate probe (include/attn_probe.h): a measurement aid, not part of the attention path.
 attn_status_t attn_mfma_probe(int32_t blocks, int32_t iters, float x, float y, float* out, size_t out_bytes,
                               uint64_t* ticks, size_t ticks_bytes, void* stream) {
   try {

@@ -1,6 +1,6 @@
 """C-ABI contract tests that need no GPU.
 
-The library must load, export every entry point include/attn.h declares, and
+The library must load, export every entry point include/*.h declares, and
 decline every host-knowable problem before any HIP call, with a status code and
 a reason (pull request 3705, section Execution and supported scope: alignment,
 capacity and overlap are validated before launch; pull request 3527, Notes for
@@ -28,7 +28,8 @@ def L(lib_path):
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src)))
 

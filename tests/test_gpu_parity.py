@@ -6,9 +6,14 @@ Two kinds of cases:
     {no mask, causal top-left, causal bottom-right} x {MHA, GQA} x {square,
     Sq < Skv, Sq > Skv (bottom-right then has empty rows)}, plus packed (THD)
     batches with lengths from 1 to 300 and unequal query/key lengths;
-  * the six full-size workloads (the sizes bench.py times, in the same launch
+  * the full-size workloads (the sizes bench.py times, in the same launch
     configuration), compared on sampled (sequence, kv-head) units that the oracle
-    computes one at a time, plus finiteness of every output element.
+    computes one at a time. Every output buffer starts as NaN, and every element of
+    every output must be written and finite, so a tile that is never written, or is
+    written to another unit's place, fails even where no unit is sampled. The samples
+    cover every residue of the unit index modulo 8 (the hardware deals workgroup i to
+    XCD i % 8, and the launch order rotates units over XCDs and shader engines) and
+    the last unit.
 Acceptance is in parity_util.compare.
 """
 
@@ -18,7 +23,7 @@ import torch
 
 from scaled_dot_product_02_amd.workloads import WORKLOADS, make_inputs, small
 
-from parity_util import all_units, check_units, gpu_run, run_and_check
+from parity_util import all_units, assert_all_written, check_units, gpu_run, run_and_check
 
 pytestmark = pytest.mark.gpu
 
@@ -70,33 +75,65 @@ def test_packed_sweep(d, dtype, mask, lens):
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
 
 
-# Full-size workloads: sampled units (sequence, kv-head) that the oracle computes whole.
+# Full-size workloads: sampled units (sequence, kv-head) that the oracle computes whole. For the dense
+# MHA workloads the unit index b * Hkv + g is also the query-side unit of the forward and the dQ pass;
+# the samples take one unit per residue modulo 8 and the last unit.
+def _residue_units(nseq, hkv, extra=()):
+    """One (b, g) per residue of u = b * hkv + g modulo 8, spread over the index range, plus the last."""
+    n = nseq * hkv
+    picks = {n - 1, *extra}
+    for r in range(8):
+        if r < n:
+            u = r + 8 * ((n // 8) * r // 8)  # residue r, moved further along for each r
+            picks.add(min(u, n - 1 - ((n - 1 - r) % 8)))
+    return sorted({(u // hkv, u % hkv) for u in picks})
+
+
 FULL_UNITS = {
-    "tiny": None,                  # everything
-    "dense_d128": [(1, 5)],
-    "thd_d128": "longest+shortest",
-    "dense_d512": [(0, 1)],
-    "cp_share_d256": [(0, 6)],
-    "cp_share_d512": [(0, 3)],
-    "window_d256": [(0, 2)],
-    "asym_d192": [(0, 11)],
-    "short_d128": [(0, 0), (63, 7), (127, 15)],
+    "tiny": None,                   # everything
+    "dense_d128": "residues",
+    "thd_d128": "residues+longest+shortest",
+    "dense_d512": [(0, 1), (0, 3)],  # 2 of the 4 kv-heads, the last included
+    "cp_share_d256": [(0, 2), (0, 7)],
+    "cp_share_d512": [(0, 3), (0, 7)],
+    "window_d256": [(0, 2), (0, 7)],
+    "asym_d192": [(0, 11), (1, 15)],
+    "short_d128": "residues",
 }
+
+
+def _full_units(name, w, x):
+    units = FULL_UNITS[name]
+    if units is None:
+        return all_units(w, x)
+    if isinstance(units, list):
+        return units
+    nseq = len(x["seqlens_q"])
+    extra = ()
+    if "longest" in units:
+        lens = x["seqlens_q"]
+        extra = (lens.index(max(lens)) * w.hkv + 3, lens.index(min(lens)) * w.hkv + 0)
+    return _residue_units(nseq, w.hkv, extra)
+
+
+def test_residue_units_cover_every_xcd_and_the_last_unit():
+    for nseq, hkv in ((2, 16), (16, 8), (128, 16), (1, 4), (3, 3)):
+        units = _residue_units(nseq, hkv)
+        idx = {b * hkv + g for b, g in units}
+        assert nseq * hkv - 1 in idx
+        assert {u % 8 for u in idx} == set(range(min(8, nseq * hkv)))
+        assert all(0 <= b < nseq and 0 <= g < hkv for b, g in units)
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_full_workload(name):
     w = WORKLOADS[name]
     x = make_inputs(w)
+    print(f"full workload {name}: {w.note}", flush=True)
     got = gpu_run(w, x)
-    for n, t in got.items():
-        assert torch.isfinite(t).all(), f"{name}: non-finite values in {n}"
-    units = FULL_UNITS[name]
-    if units is None:
-        units = all_units(w, x)
-    elif units == "longest+shortest":
-        lens = x["seqlens_q"]
-        units = [(lens.index(max(lens)), 3), (lens.index(min(lens)), 0)]
+    assert_all_written(name, got)
+    units = _full_units(name, w, x)
+    print(f"  units compared: {units}", flush=True)
     ok, msgs = check_units(w, x, got, units)
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
 

@@ -17,8 +17,12 @@ this engine's target: 2e-2 (bf16) / 5e-3 (fp16) on O, dQ, dK, dV and 1e-3 on LSE
   rounding midpoint lands on the other neighbour, one spacing away. Below
   |ref| = 4 (bf16) / 8 (fp16) that spacing is under B and the literal bound B
   applies unchanged; above it no stored value can meet B (bf16 values in
-  [8, 16) are 1/16 apart), so one spacing is the bound there. The literal
-  max-abs error and whether it meets B are printed for every tensor.
+  [8, 16) are 1/16 apart), so one spacing is the bound there. Where the
+  floor itself misses that bound (long reductions of dtype-rounded terms, e.g.
+  dQ of a D=256 GQA case with hundreds of keys, where the in-dtype computation
+  is 2.6 spacings off at |ref| = 1.1), the kernel must instead be no less
+  accurate than the floor (err <= 1 x floor). The literal max-abs error and
+  whether it meets B are printed for every tensor.
 Rows whose oracle LSE is -inf (no allowed key) must be -inf exactly and are
 left out of the LSE errors.
 """
@@ -142,13 +146,19 @@ def compare(name, got, ref, flo, dtype, is_lse=False):
     err_f = float(np.abs(flo - ref).max())
     lim = fixed_bound(ref, dtype, is_lse)
     worst = float((diff / lim).max())  # <= 1 passes the fixed bound
+    floor_worst = float((np.abs(flo - ref) / lim).max())
     lit = LSE_BOUND if is_lse else BOUND[dtype]
     slack = 1e-6 * max(1.0, float(np.abs(ref).max()))
-    ok = worst <= 1.0 and err_k <= 2 * err_f + slack
+    # Where the in-dtype computation itself misses the fixed bound (long reductions of dtype-rounded
+    # terms: dQ, dK, dV near |ref| ~ 1 with hundreds of keys), no kernel that rounds as the method does can
+    # meet it; there the kernel must be at least as accurate as that computation (1 x floor, not 2 x).
+    fixed_ok = worst <= 1.0 or (floor_worst > 1.0 and err_k <= err_f + slack)
+    ok = fixed_ok and err_k <= 2 * err_f + slack
     rel_rms = float(np.sqrt(np.mean((got - ref) ** 2)) / max(np.sqrt(np.mean(ref ** 2)), 1e-30))
     err_u = float((diff / np.maximum(1.0, np.abs(ref))).max())
     return ok, (f"{name}: err={err_k:.3e} literal<={lit:.0e}:{'yes' if err_k <= lit else 'no'} "
                 f"floor={err_f:.3e} ratio={err_k / max(err_f, 1e-30):.2f} fixed={worst:.2f} "
+                f"{'(floor fixed=' + format(floor_worst, '.2f') + ') ' if worst > 1.0 else ''}"
                 f"err/max(1,|ref|)={err_u:.3e} max|ref|={float(np.abs(ref).max()):.2f} relrms={rel_rms:.2e}")
 
 

@@ -9,7 +9,7 @@ dtypes themselves: the next representable value after x lies ulp(x) above it.
 import numpy as np
 import torch
 
-from parity_util import BOUND, fixed_bound, ulp
+from parity_util import BOUND, compare, fixed_bound, ulp
 
 
 def test_spacings():
@@ -33,3 +33,23 @@ def test_bounds_literal_below_the_crossover_and_one_spacing_above():
     f = fixed_bound(np.array([7.9, 8.0, 20.0]), "fp16")
     assert f[0] == BOUND["fp16"] and f[1] == 2 ** -7 and f[2] == 2 ** -6
     assert (fixed_bound(np.array([1.0, 50.0]), "bf16", is_lse=True) == 1e-3).all()
+
+
+def test_compare_fixed_bound_and_floor_rules():
+    ref = np.array([1.1, 0.5, -9.0])
+    bump = np.array([0.0205, 0.0, 0.0])
+    # over the literal bound where the floor is over it too and no more accurate: passes (1 x floor)
+    assert compare("t", ref + bump, ref, ref + bump, "bf16")[0]
+    # the same error where the floor meets the bound: fails
+    assert not compare("t", ref + bump, ref, ref + np.array([0.019, 0, 0]), "bf16")[0]
+    # under the bound but more than twice the floor's error: fails
+    assert not compare("t", ref + np.array([0.01, 0, 0]), ref, ref + np.array([0.004, 0, 0]), "bf16")[0]
+    # one bf16 spacing (1/16) allowed at |ref| = 9, not more
+    assert compare("t", ref + np.array([0, 0, 0.06]), ref, ref + np.array([0, 0, 0.05]), "bf16")[0]
+    assert not compare("t", ref + np.array([0, 0, 0.07]), ref, ref + np.array([0, 0, 0.05]), "bf16")[0]
+    # unwritten (NaN) elements fail
+    assert not compare("t", np.array([np.nan, 0.5, -9.0]), ref, ref, "bf16")[0]
+    # LSE: -inf rows must match exactly, others within 1e-3
+    lref = np.array([-np.inf, 2.0])
+    assert compare("l", np.array([-np.inf, 2.0005]), lref, np.array([-np.inf, 2.0004]), "bf16", is_lse=True)[0]
+    assert not compare("l", np.array([0.0, 2.0]), lref, lref, "bf16", is_lse=True)[0]

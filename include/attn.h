@@ -184,6 +184,20 @@ attn_status_t attn_bwd_dq_preprocess(const attn_problem_t* p, const void* q, con
                                      const void* o, const void* d_o, const float* lse, void* dq, void* dk,
                                      void* dv, void* ws, size_t ws_bytes, void* stream);
 
+/* The backward without a caller workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, validation,
+ * kernels and results as attn_bwd (bitwise), except that the workspace is a library-owned device array
+ * of ATTN_NOALLOC_MAX_WORKSPACE bytes that each GPU the library runs on holds from the first call until
+ * the process ends; its device address is looked up once per device. Nothing is allocated or freed.
+ * A problem whose attn_bwd_workspace_bytes() exceeds ATTN_NOALLOC_MAX_WORKSPACE (more than about 2M
+ * query rows x heads) is declined with ATTN_E_WORKSPACE before any HIP call. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (different streams without ordering
+ * between them) race on it and must not be issued; calls ordered on one stream are safe. The array
+ * keeps the last call's contents; nothing in it has to start at zero. */
+#define ATTN_NOALLOC_MAX_WORKSPACE (16u << 20)
+attn_status_t attn_bwd_noalloc(const attn_problem_t* p, const void* q, const void* k, const void* v, const void* o,
+                               const void* d_o, const float* lse, void* dq, void* dk, void* dv, void* stream);
+
 /* Merge of attention results over disjoint key chunks: the combination step of the p2p (ring)
  * context-parallel mode, which shards the keys across steps (pull request 3527, section Scope), with
  * neutral statistics for empty blocks (pull request 3693, Description). o_parts[k], lse_parts[k]

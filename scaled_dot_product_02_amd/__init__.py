@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     AttnProblem,
     attn_bwd,
+    attn_bwd_noalloc,
     attn_bwd_workspace_bytes,
     attn_fwd,
     attn_fwd_workspace_bytes,

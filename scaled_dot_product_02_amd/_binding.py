@@ -19,7 +19,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess",
-            "attn_merge", "attn_mfma_probe",
+            "attn_bwd_noalloc", "attn_merge", "attn_mfma_probe",
             "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
             "attn_abi_version")
 MERGE_MAX_PARTS = 8
@@ -84,6 +84,8 @@ def lib():
         for name in BWD_PASSES.values():
             getattr(L, name).argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             getattr(L, name).restype = ctypes.c_int
+        L.attn_bwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_bwd_noalloc.restype = ctypes.c_int
         L.attn_merge.argtypes = [pp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
         L.attn_merge.restype = ctypes.c_int
         L.attn_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, vp, sz, vp, sz,
@@ -323,6 +325,36 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes, sptr)
         if st != 0:
             _raise(st)
+    return dq, dk, dv
+
+
+NOALLOC_MAX_WORKSPACE = 16 << 20  # ATTN_NOALLOC_MAX_WORKSPACE
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None,
+                     max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, stream=None, window_left=-1):
+    """attn_bwd_noalloc through the C-ABI: attn_bwd with the library's own per-device scratch array as the
+    workspace (no workspace argument; problems needing more than NOALLOC_MAX_WORKSPACE bytes are declined).
+    Returns (dQ, dK, dV); dQ/dK/dV are allocated here unless given (the library allocates nothing)."""
+    import torch
+    _check_tensors(q, k, v, cu_seqlens_q is not None, cu_seqlens_q, cu_seqlens_kv, o=o, do=do, lse=lse, dq=dq,
+                   dk=dk, dv=dv)
+    if do.stride() != o.stride():
+        raise ValueError("dO must have the same strides as O")
+    if dq is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if dk is None:
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    if dv is None:
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("dQ/dK/dV must have the strides of Q/K/V")
+    p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
+                     window_left)
+    st = lib().attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                _ptr(dk), _ptr(dv), _stream(stream))
+    if st != 0:
+        _raise(st)
     return dq, dk, dv
 
 

@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
-SOURCES = ["attn_kernels.hip", "attn_probe.hip", "attn_abi.cpp"]
+SOURCES = ["attn_kernels.hip", "attn_probe.hip", "attn_noalloc.hip", "attn_abi.cpp"]
 
 
 def _compile(src, obj, extra):

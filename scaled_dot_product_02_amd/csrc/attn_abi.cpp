@@ -231,6 +231,11 @@ sdpa::TensorAddr lse_addr(const attn_problem_t* p, bool packed) {
 
 }  // namespace
 
+int sdpa::fail_status_code(int s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
 extern "C" {
 
 int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }

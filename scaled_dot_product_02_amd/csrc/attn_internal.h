@@ -87,6 +87,9 @@ int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
 int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsigned long long* ticks,
                       void* stream);
 int fwd_query_tile(int head_dim);
+// Records the reason attn_last_error() returns on this thread and returns s (attn_abi.cpp); for entry
+// points defined in other sources.
+int fail_status_code(int s, const char* msg);
 int bwd_key_tile(int head_dim);
 int bwd_query_tile(int head_dim);
 

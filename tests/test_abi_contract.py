@@ -389,3 +389,19 @@ def test_every_backward_entry_point_validates(L, entry):
     expect(L, call(p, ws_bytes=need - 256), WORKSPACE, "workspace")
     expect(L, call(p, dq=DQ + 2), ALIGN, "dq")
     expect(L, call(p, dq=DK), OVERLAP, "overlap")
+
+
+def test_noalloc_declines_before_any_hip_call(L):
+    """attn_bwd_noalloc checks the problem and its workspace need against ATTN_NOALLOC_MAX_WORKSPACE on the
+    host, before it looks up its device array or launches anything."""
+    def call(p):
+        return L.attn_bwd_noalloc(ctypes.byref(p), Q, K, V, O, DO, LSE, DQ, DK, DV, None)
+
+    bad = dense_problem()
+    bad.head_dim = 100
+    expect(L, call(bad), UNSUPPORTED, "head_dim 100")
+    big = dense_problem(b=2, sq=262144, skv=64, hq=8, hkv=8, d=64)  # 2 x 262144 x 8 rows x 8 bytes = 32 MiB
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(big)) > B.NOALLOC_MAX_WORKSPACE
+    expect(L, call(big), WORKSPACE, "attn_bwd_noalloc holds")
+    fits = dense_problem(b=1, sq=131072, skv=64, hq=15, hkv=15, d=64)  # 15 MiB of rows: inside the array
+    assert 0 < L.attn_bwd_workspace_bytes(ctypes.byref(fits)) <= B.NOALLOC_MAX_WORKSPACE

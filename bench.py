@@ -115,7 +115,8 @@ def flop_per_pair(w):
     per kernel: the dK/dV pass S, dP, dV, dK and the dQ pass its dQ product (its second S/dP recompute
     is executed but not credited)."""
     dqk, dv = w.d, w.d_v
-    return {"fwd": 2.0 * (dqk + dv), "bwd": 6.0 * dqk + 4.0 * dv, "bwd_dkdv": 4.0 * (dqk + dv), "bwd_dq": 2.0 * dqk}
+    return {"fwd": 2.0 * (dqk + dv), "bwd": 6.0 * dqk + 4.0 * dv, "bwd_dkdv": 4.0 * (dqk + dv), "bwd_dq": 2.0 * dqk,
+            "bwd_fused": 6.0 * dqk + 4.0 * dv}
 
 
 def fused_backward(w):
@@ -138,8 +139,13 @@ def compulsory_bytes(w, x, nrows):
     k, v = nkv * w.hkv * w.d * el, nkv * w.hkv * w.d_v * el
     row = nrows * w.hq * 4
     dq = q + o + k + v + q + (o + row + 2 * row if fused_backward(w) else 2 * row)
+    acc = 2 * q  # the fp32 dQ buffer of the single-pass backward (4 bytes per element)
     return {"fwd": q + k + v + o + row, "bwd_pre": 2 * o + row + 2 * row,
-            "bwd_dkdv": q + o + k + v + 2 * row + k + v, "bwd_dq": dq}
+            "bwd_dkdv": q + o + k + v + 2 * row + k + v, "bwd_dq": dq,
+            # single-pass backward: preprocess also zeroes the buffer; the fused kernel writes it once at
+            # least; the conversion reads it and writes dQ
+            "bwd_pre_zero": 2 * o + row + 2 * row + acc, "bwd_fused": q + o + k + v + 2 * row + k + v + acc,
+            "bwd_dq_convert": acc + q}
 
 
 def kernel_roofline(w, x, nrows, pairs, kern_ms):
@@ -236,7 +242,12 @@ def oracle_sample(w, x, rows=512):
             "bwd_tflops": round(fp["bwd"] * pairs / (t2 - t1) / 1e12, 5)}
 
 
-def run(w, steps, warmup, want_events=True, flush_mall=False):
+def atomic_supported(w):
+    """Whether the single-pass backward (ATTN_FLAG_BWD_ATOMIC_DQ) is built for w's head dims."""
+    return max(w.d, w.d_v) <= 128
+
+
+def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False):
     """Time `steps` steps of workload w. With flush_mall, a 512 MiB buffer is overwritten before every
     timed step (outside the per-kernel events), so no input is still in the 256 MB memory-side cache
     when a step starts; ms_step then includes the fill and only the per-kernel times are meaningful."""
@@ -264,13 +275,19 @@ def run(w, steps, warmup, want_events=True, flush_mall=False):
     fused = fused_backward(w)
     names = ["fwd", "bwd_dq", "bwd_dkdv"] if fused else ["fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"]
     seq = ["dq_preprocess", "dkdv"] if fused else ["preprocess", "dkdv", "dq"]
+    if atomic:  # single-pass backward: preprocess (+ zeroing), the fused kernel, the dQ conversion
+        names = ["fwd", "bwd_pre_zero", "bwd_fused", "bwd_dq_convert"]
+        seq = ["preprocess", "dkdv", "dq"]
+        p.flags = sd.FLAG_BWD_ATOMIC_DQ
+        wsb = torch.empty(sd.attn_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        kw["atomic_dq"] = True
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, **kw)
+        sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, **{n: a for n, a in kw.items() if n != "atomic_dq"})
         for i, pas in enumerate(seq):
             mark(1 + i)
             sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=(pas,), **kw)
@@ -430,6 +447,27 @@ def case_measure(w, steps, warmup, oracle_rows=512):
     return out
 
 
+def single_pass_measure(w, steps, warmup):
+    """The same workload with the single-pass backward (ATTN_FLAG_BWD_ATOMIC_DQ): backward ms, TFLOP/s
+    (the same credited FLOPs) and per-kernel times, the step with the default forward."""
+    r = run(w, steps, warmup, atomic=True)
+    fp = flop_per_pair(w)
+    km = r["kern_ms"]
+    bwd_ms = sum(t for n, t in km.items() if n != "fwd")
+    f_fwd, f_bwd = fp["fwd"] * r["pairs"], fp["bwd"] * r["pairs"]
+    kroof = kernel_roofline(w, r["x"], r["nrows"], r["pairs"], km)
+    return {"what": "single-pass backward (ATTN_FLAG_BWD_ATOMIC_DQ): preprocess with the zeroing of the fp32 dQ "
+                    "buffer, the dK/dV kernel that also adds dQ with fp32 atomics, the dQ conversion",
+            "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+                    "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},
+            "fwd_bwd": {"tflops": round((f_fwd + f_bwd) / ((km["fwd"] + bwd_ms) * 1e-3) / 1e12, 2),
+                        "ms_per_step": round(r["ms_step"], 4)},
+            "kernel_ms": {n: round(t, 4) for n, t in km.items()},
+            "kernel_ms_min": {n: round(t, 4) for n, t in r["kern_min"].items()},
+            "kernel_roofline": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in e.items()}
+                                for n, e in kroof.items()}}
+
+
 # The named cases timed in every default run besides the headline (dense_d128): the tiny case, the packed
 # GQA batch, the D=512 layer and the two single-rank context-parallel shares.
 CASES = ("tiny", "thd_d128", "dense_d512", "cp_share_d256", "cp_share_d512")
@@ -442,6 +480,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-pass-only", action="store_true",
+                    help="time only the workload with the single-pass backward and print its line")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other named cases and the informational merge and short-sequence lines")
     ap.add_argument("--merge-only", action="store_true",
@@ -476,6 +516,10 @@ def main():
         print(json.dumps({"merge": merge_measure(w, steps=args.steps, warmup=args.warmup)}), flush=True)
         return
     log(f"workload {w.name}: {w.note}")
+    if args.single_pass_only:
+        print(json.dumps({"workload": w.name, "single_pass": single_pass_measure(w, args.steps, args.warmup)}),
+              flush=True)
+        return
     tele_before = telemetry() if not args.no_extra else None
     r = run(w, args.steps, args.warmup)
     tele_after = telemetry() if not args.no_extra else None
@@ -519,12 +563,17 @@ def main():
         out["telemetry"] = {"before": tele_before, "after": tele_after}
         out["sustained_mfma"] = mfma_probe_measure()
         out["hbm_copy"] = copy_rate()
+    if not args.no_extra and atomic_supported(w):
+        log("single-pass backward on the same workload")
+        out["single_pass"] = single_pass_measure(w, args.steps, args.warmup)
     if not args.no_extra and w.name == "dense_d128":
         out["cases"] = {}
         for name in CASES:
             wc = WORKLOADS[name]
             log(f"case {name}: {wc.note}")
             out["cases"][name] = case_measure(wc, max(5, args.steps // 2), 3)
+            if atomic_supported(wc):
+                out["cases"][name]["single_pass"] = single_pass_measure(wc, max(5, args.steps // 2), 3)
         out["extra"] = {"merge": merge_measure(w)}
         w3 = WORKLOADS["short_d128"]
         r3 = run(w3, max(5, args.steps // 3), 3)

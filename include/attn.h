@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
@@ -118,7 +118,21 @@ typedef struct attn_problem {
   int64_t o_stride[3];
   int32_t window_left; /* sliding window below the causal diagonal (see above); -1 = none (ABI 2) */
   int32_t head_dim_v;  /* D_v: head dim of V, O (multiple of 8 in [8, 512]); 0 = head_dim (ABI 3) */
+  int32_t flags;       /* ATTN_FLAG_* bits; 0 = the defaults (ABI 4)                         */
 } attn_problem_t;
+
+/* Single-pass backward (pull request 3527, section Scope: the backward there has no deterministic mode at
+ * all; this engine's default backward is deterministic and this flag trades that for speed). With the flag
+ * the dK/dV pass also forms dQ += scale * dS K for its key tile and adds it with fp32 atomics into a
+ * workspace buffer, so the scores and dP are computed once per allowed pair instead of twice (the default
+ * dQ pass recomputes them). dQ then depends on the order of those additions: results agree with the
+ * default backward to fp32 rounding, not bit for bit. Head dims up to 128 (both head_dim and head_dim_v);
+ * wider heads are ATTN_E_UNSUPPORTED. The workspace grows by 4 * head_dim bytes per query row and q-head.
+ * The forward ignores the flag. With it, the backward passes are: attn_bwd_preprocess (D, LSE in log2
+ * units, and the zeroing of the dQ buffer), attn_bwd_dkdv (dK, dV and the dQ accumulation) and attn_bwd_dq
+ * (dQ = the scaled buffer rounded to dtype), in that order; attn_bwd runs the three;
+ * attn_bwd_dq_preprocess is ATTN_E_UNSUPPORTED. */
+#define ATTN_FLAG_BWD_ATOMIC_DQ 1
 
 /* Workspace (pull request 3705, section Execution and supported scope: the caller binds the workspace
  * on every call; pull request 3527, section Known limitations: the backward workspace there grows
@@ -130,7 +144,8 @@ typedef struct attn_problem {
  * keys), so no pre-clearing is needed and a stale word from another call is never trusted. Dense
  * calls neither read nor write it. Dense forward calls need no workspace (0 bytes; ws may be NULL).
  * The backward workspace is linear in the number of query tokens: header + two fp32 [Hq x tokens]
- * arrays (row sums D = rowsum(dO * O), and LSE in log2 units). Sizes are multiples of 256. */
+ * arrays (row sums D = rowsum(dO * O), and LSE in log2 units), and with ATTN_FLAG_BWD_ATOMIC_DQ an fp32
+ * [tokens x Hq x head_dim] dQ buffer. Sizes are multiples of 256. */
 size_t attn_fwd_workspace_bytes(const attn_problem_t* p);
 size_t attn_bwd_workspace_bytes(const attn_problem_t* p);
 

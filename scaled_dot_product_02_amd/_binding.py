@@ -14,7 +14,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_NAME = "libsdpa02.so"
 
-ABI_VERSION = 3
+ABI_VERSION = 4
+FLAG_BWD_ATOMIC_DQ = 1  # ATTN_FLAG_BWD_ATOMIC_DQ
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
@@ -50,6 +51,7 @@ class AttnProblem(ctypes.Structure):
         ("o_stride", ctypes.c_int64 * 3),
         ("window_left", ctypes.c_int32),
         ("head_dim_v", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -201,7 +203,7 @@ def _check_tensors(q, k, v, packed, cu_seqlens_q=None, cu_seqlens_kv=None, o=Non
 
 
 def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                 window_left=-1):
+                 window_left=-1, flags=0):
     packed = cu_seqlens_q is not None
     p = AttnProblem()
     p.abi_version = ABI_VERSION
@@ -231,6 +233,7 @@ def make_problem(q, k, v, o_like, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_
     p.v_stride[:] = _strides(v, packed)
     p.o_stride[:] = _strides(o_like, packed)
     p.window_left = int(window_left)
+    p.flags = int(flags)
     return p
 
 
@@ -291,14 +294,15 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
 
 def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None,
              max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
-             passes=("all",), window_left=-1):
+             passes=("all",), window_left=-1, atomic_dq=False):
     """Backward through the C-ABI from the forward's O and LSE. Returns (dQ, dK, dV).
 
     dO must have O's strides; dQ/dK/dV are allocated with Q/K/V's shapes (contiguous) unless given.
     ``passes`` lists the entry points to call in order: "all" (attn_bwd) or any of "preprocess",
     "dkdv", "dq", "dq_preprocess" (attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq /
     attn_bwd_dq_preprocess, which share the workspace; "dq_preprocess" then "dkdv" is what
-    attn_bwd runs for head dims up to 256).
+    attn_bwd runs for head dims up to 256). ``atomic_dq`` sets ATTN_FLAG_BWD_ATOMIC_DQ (the single-pass
+    backward, head dims up to 128): then "preprocess", "dkdv", "dq" is what attn_bwd runs.
     """
     import torch
     _check_tensors(q, k, v, cu_seqlens_q is not None, cu_seqlens_q, cu_seqlens_kv, o=o, do=do, lse=lse, dq=dq,
@@ -314,7 +318,7 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("dQ/dK/dV must have the strides of Q/K/V")
     p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                     window_left)
+                     window_left, FLAG_BWD_ATOMIC_DQ if atomic_dq else 0)
     L = lib()
     need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
     ws = _workspace(need, q.device, workspace)

@@ -108,6 +108,7 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (!(p->scale > 0.f)) return fail(ATTN_E_UNSUPPORTED, "scale %g is not positive", (double)p->scale);
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
   if (p->window_left < -1) return fail(ATTN_E_INVALID, "window_left %d < -1", p->window_left);
+  if (p->flags & ~ATTN_FLAG_BWD_ATOMIC_DQ) return fail(ATTN_E_INVALID, "unknown flags 0x%x", (unsigned)p->flags);
   if (p->window_left >= 0 && p->mask == ATTN_MASK_NONE)
     return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
                 p->window_left);
@@ -264,7 +265,9 @@ size_t attn_fwd_workspace_bytes(const attn_problem_t* p) {
 size_t attn_bwd_workspace_bytes(const attn_problem_t* p) {
   Info in;
   if (check_problem(p, &in) != ATTN_OK) return 0;
-  return kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float));
+  size_t n = kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float));
+  if (p->flags & ATTN_FLAG_BWD_ATOMIC_DQ) n += round256((size_t)in.nq * p->heads_q * p->head_dim * sizeof(float));
+  return n;
 }
 
 attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -367,6 +370,13 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     }
     for (int i = 0; i < 6; ++i)
       if (overlaps(ew, *ins[i])) return fail(ATTN_E_OVERLAP, "workspace overlaps an input");
+    const bool atomic = (p->flags & ATTN_FLAG_BWD_ATOMIC_DQ) != 0;
+    if (atomic && (dqk > 128 || dvw > 128))
+      return fail(ATTN_E_UNSUPPORTED, "the single-pass backward (ATTN_FLAG_BWD_ATOMIC_DQ) is built for head dims up "
+                  "to 128; head_dim %d, head_dim_v %d", dqk, dvw);
+    if (atomic && passes == sdpa::kPassDqPre)
+      return fail(ATTN_E_UNSUPPORTED, "attn_bwd_dq_preprocess has no single-pass form (ATTN_FLAG_BWD_ATOMIC_DQ): "
+                  "call attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq");
     sdpa::BwdArgs a{};
     const int inst = sdpa::instance_head_dim(dqk, dvw);
     a.s = make_shape(p, in, ws, sdpa::bwd_query_tile(inst));
@@ -388,6 +398,9 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     a.nrows = in.nq;
     a.rowsum = (float*)((char*)ws + kHeader);
     a.lse2 = (float*)((char*)ws + kHeader + round256((size_t)in.nq * p->heads_q * sizeof(float)));
+    a.atomic_dq = atomic ? 1 : 0;
+    a.dq_acc = atomic ? (float*)((char*)ws + kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float)))
+                      : nullptr;
     a.aq = addr(p->q_stride, in.packed);
     a.ak = addr(p->k_stride, in.packed);
     a.av = addr(p->v_stride, in.packed);

@@ -56,6 +56,8 @@ struct BwdArgs {
   int64_t nrows;  // dense: batch * sq; packed: total_q
   TensorAddr aq, ak, av, ao, alse;
   int32_t n_kvtiles;  // ceil(skv / key tile) of the dK/dV kernel
+  int32_t atomic_dq;  // single-pass backward: dQ accumulated in dq_acc with fp32 atomics
+  float* dq_acc;      // workspace (atomic_dq only): fp32 [nrows][hq][dqk]
 };
 
 // Merge of per-chunk results (attn_merge): nrows = query rows * hq independent (row, head) pairs.
@@ -80,6 +82,8 @@ int launch_validate_cu(const AttnShape& s, void* stream);
 int launch_fwd(int dtype, int head_dim, const FwdArgs& a, void* stream);
 // Backward passes selected by bit: 1 = preprocess, 2 = dK/dV pass, 4 = dQ pass, 8 = the dQ pass with
 // the preprocess folded in (the same as 1 | 4). Preprocess and dQ together run fused for D <= 256.
+// With a.atomic_dq (head dims up to 128): 1 = preprocess with the zeroing of dq_acc, 2 = the single-pass
+// kernel (dK, dV and the atomic dQ accumulation), 4 = the conversion of dq_acc into dQ; 8 is not used.
 enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassDqPre = 8, kPassAll = 7 };
 int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream);
 int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);

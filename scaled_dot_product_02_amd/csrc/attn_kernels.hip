@@ -1425,6 +1425,408 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Single-pass backward (opt-in, ATTN_FLAG_BWD_ATOMIC_DQ), head dims up to 128. The dK/dV pass also
+// forms dQ += scale * dS K for its key tile and adds it with fp32 atomics into a workspace buffer
+// (dq_acc, zeroed by the preprocess, scaled and rounded by attn_bwd_dq_convert_kernel), so S and dP are
+// computed once per allowed pair instead of twice: 10*D FLOP executed per pair instead of 14*D. The
+// order in which key tiles add into a dQ row is not fixed, so dQ is not bitwise deterministic in this
+// mode (the pages' own backward has no deterministic mode either: pull request 3527, section Scope).
+//
+// Workgroup = 8 waves = 128 keys of one (sequence, kv-head); wave pair (p, p + 4) owns 32 keys (two
+// 16-key blocks). Wave p (role 0) holds their K and computes S = Q K^T, P = exp2(S*c - lse2), hands P
+// (fp32) to its partner through LDS and accumulates dV += P^T dO. Wave p + 4 (role 1) holds V, computes
+// dP = dO V^T, takes P, forms dS = P (dP - D), writes dS (rounded to T) into LDS and accumulates
+// dK += dS^T Q. Query tiles of 64 rows stream through LDS (Q, dO, lse2, D). The dQ product of a tile
+// needs every pair's dS, so it runs one iteration later, after the barrier that starts the next tile:
+// wave w takes query rows 32*(w/4) .. +31 of the previous tile and d-columns 16*DBW*(w%4) .. over all
+// 128 keys (A = dS by transpose reads of the [key][row] LDS buffer, B = its K columns, held in registers
+// with lane = column, 8 keys per lane), then adds the 32 x 16*DBW result into dq_acc with vector
+// atomics (one instruction covers 4 rows x 16 consecutive floats). The roles interleave so that one
+// wave's matrix products overlap the other's vector work on the same SIMD:
+//   role 0:  S -> P -> LDS  | barrier |  dQ(prev) -> dV
+//   role 1:  dP -> dQ(prev) | barrier |  dS -> LDS -> dK
+// dS is double-buffered in LDS (the dQ product of tile t reads buffer t&1 while dS of tile t+1 goes to
+// the other buffer); P is single-buffered (written after one barrier, read before the next).
+// dS buffer layout: row = key (128), 64 row elements = 16 chunks of 4 (8 bytes); chunk c of key row r is
+// stored at chunk c ^ (((r >> 1) & 3) << 2), so both the dS writes (16 consecutive keys x 4 consecutive
+// chunks per instruction) and the transpose reads (the same shape) spread over all banks.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int ds_chunk_off(int key, int chunk) {  // element offset in one dS buffer
+  return key * 64 + ((chunk ^ (((key >> 1) & 3) << 2)) << 2);
+}
+
+__device__ __forceinline__ void atomic_add_f32(float* p, float v) {
+  __builtin_amdgcn_global_atomic_fadd_f32((__attribute__((address_space(1))) float*)p, v);
+}
+
+template <int D, typename T, bool PAD>
+__global__ void __launch_bounds__(512, 1) attn_bwd_fused_kernel(BwdArgs a) {
+  static_assert(D == 64 || D == 128, "the single-pass backward is built for head dims up to 128");
+  constexpr int NW = 8, KW = 32, BKV = 4 * KW, BQ = 64, NDB = D / 16, DBW = NDB / 4;
+  constexpr int QTILE = BQ * D;
+  constexpr int NDMA = QTILE * 2 / 1024 / NW;
+  static_assert(NDMA >= 1, "query tile must split over 8 waves");
+  constexpr int STAGE = 2 * QTILE + 2 * 64 * 2;  // Q, dO tiles, then lse2[64] and D[64] as floats
+  __shared__ __attribute__((aligned(1024))) us smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float pbuf[4 * 8 * 64 * 4];  // P per pair: [pair][m][kb][lane][4]
+  __shared__ __attribute__((aligned(16))) us dsbuf[2 * BKV * BQ];      // dS, two buffers of [key][row]
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<T>(a.dk, a.ak, s.total_kv, s.hkv, s.dqk);
+    fill_nan_rows<T>(a.dv, a.av, s.total_kv, s.hkv, s.dv);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int pr = w & 3, role = w >> 2;
+  const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
+  int u, kt;
+  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
+  const int b = u / s.hkv, g = u % s.hkv;
+  const Seq sq = seq_info(s, b);
+  const int k0 = kt * BKV;
+  if (k0 >= sq.skv) return;
+  const int kw0 = k0 + pr * KW;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int q_lo = s.mask != 0 ? max(0, k0 - delta) : 0;
+  const int qt0 = q_lo / BQ;
+  const int q_hi = s.wl >= 0 ? k0 + BKV - 1 - delta + s.wl : sq.sq - 1;
+  const int nq = q_hi < 0 ? 0 : max(0, min((sq.sq + BQ - 1) / BQ, q_hi / BQ + 1) - qt0);
+  const int n_it = nq * s.group;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
+
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const us* vg = (const us*)a.v + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head;
+  // role 0 keeps K, role 1 keeps V (B operands of S / dP: key kw0 + 16kb + l16, d = 32kk + 8G + t)
+  v8s kvf[2][D / 32];
+  {
+    const us* src = role == 0 ? kg : vg;
+    const int64_t srow = role == 0 ? a.ak.row : a.av.row;
+    const int sd = role == 0 ? s.dqk : s.dv;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int64_t r = min(kw0 + 16 * kb + l16, sq.skv - 1);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) kvf[kb][kk] = ld_chunk<PAD>(src + r * srow + 32 * kk + 8 * G, 32 * kk + 8 * G, sd);
+    }
+  }
+  // K columns for the dQ product (B operand, lane = column d, 8 keys per lane): d block db0 + j, key
+  // chunk kc: slot t < 4 holds key k0 + 32kc + 4G + t, slot t >= 4 key k0 + 32kc + 16 + 4G + t - 4 (the
+  // key order of the transpose reads of dS)
+  const int dqh = w >> 2, db0 = (w & 3) * DBW;
+  v8s kq[DBW][4];
+#pragma unroll
+  for (int j = 0; j < DBW; ++j) {
+    const int d = 16 * (db0 + j) + l16;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int key = k0 + 32 * kc + (t < 4 ? 4 * G + t : 16 + 4 * G + t - 4);
+        const int64_t r = min(key, sq.skv - 1);
+        kq[j][kc][t] = (PAD && d >= s.dqk) ? (short)0 : (short)kg[r * a.ak.row + d];
+      }
+  }
+  v4f acc[2][NDB];  // role 0: dV, role 1: dK; key kw0 + 16kb + 4G + i, column 16dt + l16
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int dt = 0; dt < NDB; ++dt) acc[kb][dt] = v4f{};
+
+  const TileDma<D, BQ, NDMA, true, PAD> dma(w, lane, a.aq.row, a.ao.row, s.dqk, s.dv);
+  QueryWalk<BQ> ld(a, packed, b, sq, g * s.group, qt0, nq);
+  const int qt_end = qt0 + nq;
+  auto issue = [&](int stage) {
+    const int qs0 = ld.qt * BQ;
+    us* qs = smem + stage * STAGE;
+    us* dos = qs + QTILE;
+    float* l2s = reinterpret_cast<float*>(dos + QTILE);
+    float* rss = l2s + 64;
+    dma.copy(ld.qp, ld.op, sq.sq - 1 - qs0, qs, dos);
+    const int r = min(qs0 + lane, sq.sq - 1);
+    if (w == 0) dma4(ld.l2, 4u * r, l2s);
+    if (w == 1) dma4(ld.rs, 4u * r, rss);
+    ld.next();
+  };
+
+  // LDS offsets as in attn_bwd_dkdv_kernel: row reads rows 16m + l16, chunk 4kk + G; transpose reads rows
+  // 4G + rr (+16) of a 32-row half, chunk 2dt + cc/2
+  const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
+  const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
+  float* pb = pbuf + pr * 8 * 64 * 4;
+  const float scale_log2 = s.scale_log2;
+  const int64_t hqd = (int64_t)s.hq * s.dqk;
+
+  // dQ(prev) += dS(prev) K over this workgroup's keys: rows 32*dqh + 16*m2 + 4G + i of the query tile at
+  // prev_qs0 of q-head prev_h, columns 16*(db0 + j) + l16
+  auto dq_step = [&](int buf, int prev_qs0, int prev_h) {
+    const us* dsb = dsbuf + buf * BKV * BQ;
+    v4f dqa[2][DBW];
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int j = 0; j < DBW; ++j) dqa[m2][j] = v4f{};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int row = 32 * kc + 4 * G + rr, chunk = 8 * dqh + 4 * m2 + cc;
+        const int o = ds_chunk_off(row, chunk);  // row + 16 has the same swizzle
+        const v8s dsa = cat44(lds_read_tr(dsb, o), lds_read_tr(dsb, o + 16 * 64));
+#pragma unroll
+        for (int j = 0; j < DBW; ++j) dqa[m2][j] = Elem<T>::mma16(Elem<T>::cast(dsa), Elem<T>::cast(kq[j][kc]), dqa[m2][j]);
+      }
+    float* base = a.dq_acc + (rowbase + prev_qs0) * hqd + (int64_t)prev_h * s.dqk;
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = 32 * dqh + 16 * m2 + 4 * G + i;
+        if (prev_qs0 + q < sq.sq) {
+#pragma unroll
+          for (int j = 0; j < DBW; ++j) {
+            const int d = 16 * (db0 + j) + l16;
+            if (!PAD || d < s.dqk) atomic_add_f32(base + (int64_t)q * hqd + d, dqa[m2][j][i]);
+          }
+        }
+      }
+  };
+
+  int qt_c = qt0, h_c = g * s.group;  // query tile and q-head of the iteration
+  int prev_qs0 = 0, prev_h = 0;
+  if constexpr (PAD) {
+    zero_lds<2 * STAGE>(smem);
+    __syncthreads();
+  }
+  if (n_it > 0) issue(0);
+  for (int it = 0; it < n_it; ++it) {
+    wait_vmem();
+    __syncthreads();  // stage it is in LDS; dS of the previous tile is complete; P buffer is free
+    if (it + 1 < n_it) issue((it + 1) & 1);
+    const int sb = (it & 1) * STAGE;
+    const int qs0 = qt_c * BQ, hcur = h_c;
+    if (++qt_c == qt_end) {
+      qt_c = qt0;
+      ++h_c;
+    }
+    const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0) &&
+                        (s.wl < 0 || qs0 + delta - s.wl <= kw0 + KW - 1);
+    const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1) ||
+                           (s.wl >= 0 && qs0 + BQ - 1 + delta - s.wl > kw0);
+    const float* l2s = reinterpret_cast<const float*>(smem + sb + 2 * QTILE);
+    const float* rss = l2s + 64;
+    const int rb = opaque(2 * (rrow + rkey)) + 2 * sb;
+    v4f sv[4][2];  // role 0: S then P; role 1: dP then dS. Row 16m + 4G + i, key kw0 + 16kb + l16
+    // ---- phase A: S (role 0) or dP (role 1), and for role 1 the dQ product of the previous tile
+    if (active) {
+      const int src = rb + (role == 0 ? 0 : 2 * QTILE);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sv[m][kb] = v4f{};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v8s x = lds_read16_at(smem, (src ^ (64 * kk)) + 32 * m * D);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            sv[m][kb] = Elem<T>::mma16(Elem<T>::cast(x), Elem<T>::cast(kvf[kb][kk]), sv[m][kb]);
+        }
+      if (role == 0) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v4f l2 = *reinterpret_cast<const v4f*>(l2s + 16 * m + 4 * G);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[m][kb][i] = fast_exp2(sv[m][kb][i] * scale_log2 - l2[i]);
+        }
+        if (need_mask) {  // one branch per tile
+          const int ql = opaque(qs0 + 4 * G), kl = opaque(kw0 + l16);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int q = ql + 16 * m + i, key = kl + 16 * kb;
+                const bool ok = q < sq.sq && key < sq.skv && (s.mask == 0 || key <= q + delta) &&
+                                (s.wl < 0 || key >= q + delta - s.wl);
+                sv[m][kb][i] = ok ? sv[m][kb][i] : 0.f;
+              }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) *reinterpret_cast<v4f*>(pb + ((m * 2 + kb) * 64 + lane) * 4) = sv[m][kb];
+      }
+    }
+    if (role == 1 && it > 0) dq_step((it - 1) & 1, prev_qs0, prev_h);
+    __syncthreads();  // P of this tile is in LDS
+    // ---- phase B: dQ product of the previous tile and dV (role 0), or dS and dK (role 1)
+    if (role == 0 && it > 0) dq_step((it - 1) & 1, prev_qs0, prev_h);
+    us* dsw = dsbuf + (it & 1) * BKV * BQ;
+    if (role == 1) {
+      if (active) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v4f dr = *reinterpret_cast<const v4f*>(rss + 16 * m + 4 * G);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            const v4f pv = *reinterpret_cast<const v4f*>(pb + ((m * 2 + kb) * 64 + lane) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[m][kb][i] = pv[i] * (sv[m][kb][i] - dr[i]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) sv[m][kb] = v4f{};
+      }
+      // dS rounded to T, [key][row]: key pr*32 + 16kb + l16, rows 16m + 4G .. +3 (one 8-byte chunk)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          typename Elem<T>::op4 d4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d4[i] = Elem<T>::cvt(sv[m][kb][i]);
+          *reinterpret_cast<typename Elem<T>::op4*>(dsw + ds_chunk_off(pr * KW + 16 * kb + l16, 4 * m + G)) = d4;
+        }
+    }
+    if (active) {
+      // dV += P^T dO (role 0) / dK += dS^T Q (role 1), one 32-row half at a time: A = the accumulators of
+      // rows 32h .. +31 (k slots: 4G + t, then 16 + 4G + t), B = dO^T / Q^T by transpose reads
+      const int bsrc = (role == 0 ? 2 * QTILE : 0) + 2 * sb;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        typename Elem<T>::op8 pa[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          pa[kb] = pack8<T>(sv[2 * h][kb][0], sv[2 * h][kb][1], sv[2 * h][kb][2], sv[2 * h][kb][3], sv[2 * h + 1][kb][0],
+                            sv[2 * h + 1][kb][1], sv[2 * h + 1][kb][2], sv[2 * h + 1][kb][3]);
+        const int tb = opaque(2 * (trow + tkey)) + bsrc + 64 * D * h;
+#pragma unroll
+        for (int dt = 0; dt < NDB; ++dt) {
+          const int o1 = tb ^ (32 * dt);
+          const v8s bt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) acc[kb][dt] = Elem<T>::mma16(pa[kb], Elem<T>::cast(bt), acc[kb][dt]);
+        }
+      }
+    }
+    prev_qs0 = qs0;
+    prev_h = hcur;
+  }
+  if (n_it > 0) {
+    __syncthreads();  // dS of the last tile is complete
+    dq_step((n_it - 1) & 1, prev_qs0, prev_h);
+  }
+
+  T* outp = role == 0 ? (T*)a.dv + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head
+                      : (T*)a.dk + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const int64_t orow = role == 0 ? a.av.row : a.ak.row;
+  const float oscale = role == 0 ? 1.f : s.scale;
+  const int od = role == 0 ? s.dv : s.dqk;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kw0 + 16 * kb + 4 * G + i;
+      if (key < sq.skv) {
+#pragma unroll
+        for (int dt = 0; dt < NDB; ++dt)
+          if (!PAD || 16 * dt + l16 < od) outp[(int64_t)key * orow + 16 * dt + l16] = Elem<T>::cvt(acc[kb][dt][i] * oscale);
+      }
+    }
+}
+
+// Preprocess of the single-pass backward: attn_bwd_pre_kernel's D and LSE * log2(e), plus the zeroing of
+// this (row, head)'s D_qk floats of dq_acc ([rows][Hq][D_qk], fp32). HBM-bound.
+template <int D, typename T>
+__global__ void __launch_bounds__(256) attn_bwd_pre_zero_kernel(BwdArgs a) {
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) return;
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int64_t total = a.nrows * s.hq;
+  const int64_t R = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  int64_t t = 0, lofs = 0;
+  int h = 0;
+  if (R < total) {
+    t = R / s.hq;
+    h = (int)(R % s.hq);
+    int64_t oofs;
+    if (packed) {
+      oofs = t * a.ao.row + (int64_t)h * a.ao.head;
+      lofs = t * a.alse.row + (int64_t)h * a.alse.head;
+    } else {
+      const int64_t bb = t / s.sq, si = t % s.sq;
+      oofs = bb * a.ao.batch + si * a.ao.row + (int64_t)h * a.ao.head;
+      lofs = bb * a.alse.batch + si * a.alse.row + (int64_t)h * a.alse.head;
+    }
+    if (8 * c < s.dv) {
+      const v8s o8 = *reinterpret_cast<const v8s*>((const us*)a.o + oofs + 8 * c);
+      const v8s d8 = *reinterpret_cast<const v8s*>((const us*)a.d_o + oofs + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += to_f32<T>(o8[i]) * to_f32<T>(d8[i]);
+    }
+    if (8 * c < s.dqk) {  // R = t * hq + h: the dq_acc row of (t, h) starts at R * dqk
+      v4f* z = reinterpret_cast<v4f*>(a.dq_acc + R * s.dqk + 8 * c);
+      z[0] = v4f{};
+      z[1] = v4f{};
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (R < total && c == 0) {
+    a.rowsum[(int64_t)h * a.nrows + t] = acc;
+    const float l = a.lse[lofs];
+    a.lse2[(int64_t)h * a.nrows + t] = l == -__builtin_inff() ? __builtin_inff() : l * kLog2e;
+  }
+}
+
+// Last step of the single-pass backward: dQ = T(scale * dq_acc) in Q's layout. HBM-bound: reads 4 * D_qk,
+// writes 2 * D_qk bytes per (row, head). Rows no key reached keep the zeros of the preprocess.
+template <int D, typename T>
+__global__ void __launch_bounds__(256) attn_bwd_dq_convert_kernel(BwdArgs a) {
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<T>(a.dq, a.aq, s.total_q, s.hq, s.dqk);
+    return;
+  }
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int64_t R = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (R >= a.nrows * s.hq || 8 * c >= s.dqk) return;  // no barrier in this kernel
+  const int64_t t = R / s.hq;
+  const int h = (int)(R % s.hq);
+  int64_t qofs;
+  if (packed) {
+    qofs = t * a.aq.row + (int64_t)h * a.aq.head;
+  } else {
+    const int64_t bb = t / s.sq, si = t % s.sq;
+    qofs = bb * a.aq.batch + si * a.aq.row + (int64_t)h * a.aq.head;
+  }
+  const v4f* src = reinterpret_cast<const v4f*>(a.dq_acc + R * s.dqk + 8 * c);
+  const v4f x0 = src[0], x1 = src[1];
+  typename Elem<T>::op8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = Elem<T>::cvt(x0[i] * s.scale);
+    r[4 + i] = Elem<T>::cvt(x1[i] * s.scale);
+  }
+  *reinterpret_cast<typename Elem<T>::op8*>((T*)a.dq + qofs + 8 * c) = r;
+}
+
+// ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
 constexpr int kFwdBM = 128;
@@ -1498,7 +1900,8 @@ int instance_head_dim(int dqk, int dv) {
 }
 
 int fwd_query_tile(int) { return kFwdBM; }
-int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }  // 64 for the D = 512 pair kernel too
+int bwd_key_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }  // 64 for the D = 512 pair kernel too;
+                                                                             // 128 for the single-pass kernel
 int bwd_query_tile(int head_dim) { return 64 * (head_dim <= 128 ? 2 : 1); }
 
 int launch_validate_cu(const AttnShape& s, void* stream) {
@@ -1519,8 +1922,37 @@ static int fwd_t(const FwdArgs& a, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
+// Single-pass backward (a.atomic_dq; D <= 128, checked by the host): preprocess with zeroing, the fused
+// kernel, the conversion, each launched when its bit is set.
+template <int D, typename T, bool PAD>
+static int bwd_atomic_t(const BwdArgs& a, int passes, hipStream_t st) {
+  if constexpr (D > 128) {
+    return (int)hipErrorInvalidValue;
+  } else {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = a.nrows * a.s.hq;
+    const dim3 row_grid((unsigned)((rows + RPB - 1) / RPB));
+    hipError_t e = hipSuccess;
+    if ((passes & kPassPre) && rows > 0) {
+      hipLaunchKernelGGL((attn_bwd_pre_zero_kernel<D, T>), row_grid, dim3(256), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    }
+    if ((passes & kPassDkdv) && a.n_kvtiles > 0) {
+      const dim3 grid(a.s.batch * a.s.hkv * a.n_kvtiles);
+      hipLaunchKernelGGL((attn_bwd_fused_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    }
+    if ((passes & kPassDq) && rows > 0) {
+      hipLaunchKernelGGL((attn_bwd_dq_convert_kernel<D, T>), row_grid, dim3(256), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return (int)e;
+    }
+    return (int)e;
+  }
+}
+
 template <int D, typename T, bool PAD>
 static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
+  if (a.atomic_dq) return bwd_atomic_t<D, T, PAD>(a, passes, st);
   // Launches with an empty grid are skipped (e.g. no query rows: only dK = dV = 0 remain to write).
   // With D <= 256, a request for both the preprocess and the dQ pass (attn_bwd, or the fused pass on
   // its own) runs the dQ pass with the preprocess folded in, before the dK/dV pass that reads its

@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.attn_abi_version() == 3
+    assert L.attn_abi_version() == 4
     for code, name in B.STATUS.items():
         assert L.attn_status_str(code).decode() == name
     assert L.attn_status_str(42).decode() == "ATTN_E_UNKNOWN"
@@ -50,7 +50,7 @@ def test_version_and_status_strings(L):
 
 def dense_problem(b=2, sq=256, skv=256, hq=4, hkv=2, d=128, dtype=0, mask=1):
     p = B.AttnProblem()
-    p.abi_version = 3
+    p.abi_version = 4
     p.window_left = -1  # no sliding window (ctypes zero-fills, and 0 is a window)
     p.dtype, p.mask, p.scale = dtype, mask, d ** -0.5
     p.batch, p.heads_q, p.heads_kv, p.head_dim = b, hq, hkv, d
@@ -96,7 +96,9 @@ def test_null_problem(L):
 
 @pytest.mark.parametrize("field,value,want,frag", [
     ("abi_version", 2, UNSUPPORTED, "abi_version"),
-    ("abi_version", 4, UNSUPPORTED, "abi_version"),
+    ("abi_version", 3, UNSUPPORTED, "abi_version"),
+    ("abi_version", 5, UNSUPPORTED, "abi_version"),
+    ("flags", 4, INVALID, "unknown flags"),
     ("window_left", -2, INVALID, "window_left"),
     ("head_dim_v", -8, INVALID, "head_dim_v"),
     ("head_dim_v", 100, UNSUPPORTED, "head_dim_v 100"),
@@ -240,12 +242,14 @@ def test_binding_rejects_host_tensors(lib_path):
 
 
 def test_problem_struct_layout():
-    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3], window_left + head_dim_v (int32)
-    assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24 + 8
+    # attn_problem_t: 10 x int32, 2 pointers, 2 x int64, 4 x int64[3], window_left, head_dim_v, flags (int32),
+    # padded to the 8-byte alignment of its int64 members
+    assert ctypes.sizeof(B.AttnProblem) == 40 + 16 + 16 + 4 * 24 + 12 + 4
     assert B.AttnProblem.cu_seqlens_q.offset == 40
     assert B.AttnProblem.q_stride.offset == 72
     assert B.AttnProblem.window_left.offset == 168
     assert B.AttnProblem.head_dim_v.offset == 172
+    assert B.AttnProblem.flags.offset == 176
 
 
 def test_window_needs_a_causal_mask(L):
@@ -405,3 +409,23 @@ def test_noalloc_declines_before_any_hip_call(L):
     expect(L, call(big), WORKSPACE, "attn_bwd_noalloc holds")
     fits = dense_problem(b=1, sq=131072, skv=64, hq=15, hkv=15, d=64)  # 15 MiB of rows: inside the array
     assert 0 < L.attn_bwd_workspace_bytes(ctypes.byref(fits)) <= B.NOALLOC_MAX_WORKSPACE
+
+
+def test_single_pass_backward_flag(L):
+    """ATTN_FLAG_BWD_ATOMIC_DQ: unknown bits are refused; the flag adds 4 * head_dim bytes per query row
+    and q-head to the backward workspace; head dims past 128 and the fused dQ + preprocess pass are
+    declined with a reason, before any launch."""
+    p = dense_problem()
+    p.flags = 2
+    expect(L, bwd(L, p), INVALID, "unknown flags")
+    p = dense_problem(b=2, sq=256, hq=4, d=128)
+    base = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    p.flags = B.FLAG_BWD_ATOMIC_DQ
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(p)) == base + 2 * 256 * 4 * 128 * 4
+    expect(L, L.attn_bwd_dq_preprocess(ctypes.byref(p), Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1 << 30, None),
+           UNSUPPORTED, "attn_bwd_dq_preprocess")
+    wide = dense_problem(d=256)
+    wide.flags = B.FLAG_BWD_ATOMIC_DQ
+    expect(L, bwd(L, wide), UNSUPPORTED, "head dims up to 128")
+    need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    expect(L, bwd(L, p, ws_bytes=need - 256), WORKSPACE, "workspace")

@@ -47,25 +47,35 @@ METRIC = "attention fwd+bwd TFLOP/s at D=128/512 bf16; % of MFMA bf16 peak"
 PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated against a plain device
-# copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel
-# source it was measured on: "traffic" is null once csrc/attn_kernels.hip has changed since.
+# copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
+# measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "bwd_dkdv"): {"src_sha1": "0c7c86e2dde8", "bytes": 699309987},
-    ("dense_d128", "fwd"): {"src_sha1": "0c7c86e2dde8", "bytes": 881545096},
-    ("dense_d128", "bwd_dq"): {"src_sha1": "0c7c86e2dde8", "bytes": 907839638},
+    ("dense_d128", "fwd"): {"fingerprint": "b3c9c7a7946c", "bytes": 874901969},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "904f89aa94fc", "bytes": 933682204},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "8b13bc8d8996", "bytes": 698814589},
 }
+KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
 
-def kernel_source_sha1():
+def kernel_fingerprint(kernel):
+    """sha1 prefix of what decides one kernel's code: attn_device.h, attn_internal.h, the shared part of
+    attn_kernels.hip before its first kernel, the kernel's own definition, and the tile-size helpers the
+    launchers instantiate it with."""
     import hashlib
-    path = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc", "attn_kernels.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha1(f.read()).hexdigest()[:12]
+    import re
+    csrc = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc")
+    src = open(os.path.join(csrc, "attn_kernels.hip")).read()
+    parts = [open(os.path.join(csrc, f)).read() for f in ("attn_device.h", "attn_internal.h")]
+    parts.append(src[:src.index("__global__")])
+    m = re.search(r"__global__ void[^\n]*\b" + re.escape(kernel) + r"\(.*?\n}\n", src, re.S)
+    parts.append(m.group(0) if m else "")
+    parts += re.findall(r"template <int D> constexpr int \w+\(\) \{[^\n]*\}", src)
+    return hashlib.sha1("\n".join(parts).encode()).hexdigest()[:12]
 
 
 def traffic_for(workload, kernel):
     t = TRAFFIC.get((workload, kernel))
-    return t["bytes"] if t and t["src_sha1"] == kernel_source_sha1() else None
+    return t["bytes"] if t and kernel in KERNEL_OF and t["fingerprint"] == kernel_fingerprint(KERNEL_OF[kernel]) else None
 
 
 def log(*a):

@@ -458,6 +458,55 @@ def case_measure(w, steps, warmup, oracle_rows=512):
     return out
 
 
+def graph_step_us(w, replays=50):
+    """Device time of one whole step (forward + the backward launches attn_bwd makes) captured once in a HIP
+    graph and replayed back to back: the figure that matters for a latency-bound case, where the HIP events
+    around each eager launch also hold the host-side launch path. Every buffer is allocated before capture
+    (the library allocates nothing)."""
+    import torch
+    import scaled_dot_product_02_amd as sd
+    from scaled_dot_product_02_amd.workloads import make_inputs
+    dev = torch.device("cuda:0")
+    x = make_inputs(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    kw = dict(mask=w.mask, scale=w.scale, window_left=w.window_left)
+    if w.packed:
+        kw.update(cu_seqlens_q=x["cu_seqlens_q"].to(dev), cu_seqlens_kv=x["cu_seqlens_kv"].to(dev),
+                  max_seqlen_q=x["max_seqlen_q"], max_seqlen_kv=x["max_seqlen_kv"])
+    o = torch.empty(q.shape[:-1] + v.shape[-1:], dtype=q.dtype, device=dev)
+    p = sd.make_problem(q, k, v, o, w.mask, w.scale, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_kv"),
+                        x["max_seqlen_q"], x["max_seqlen_kv"], w.window_left)
+    lse_shape = (q.shape[0], q.shape[1]) if w.packed else (q.shape[0], q.shape[2], q.shape[1])
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wsf = torch.empty(max(sd.attn_fwd_workspace_bytes(p), 256), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(sd.attn_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+
+    def step():
+        sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, **kw)
+        sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1e3 / replays, 2)
+
+
 def single_pass_measure(w, steps, warmup):
     """The same workload with the single-pass backward (ATTN_FLAG_BWD_ATOMIC_DQ): backward ms, TFLOP/s
     (the same credited FLOPs) and per-kernel times, the step with the default forward."""
@@ -583,6 +632,8 @@ def main():
             wc = WORKLOADS[name]
             log(f"case {name}: {wc.note}")
             out["cases"][name] = case_measure(wc, max(5, args.steps // 2), 3)
+            if name == "tiny":  # latency-bound: the device time of a whole step, launched as one graph
+                out["cases"][name]["graph_us_per_step"] = graph_step_us(wc)
             if atomic_supported(wc):
                 out["cases"][name]["single_pass"] = single_pass_measure(wc, max(5, args.steps // 2), 3)
         out["extra"] = {"merge": merge_measure(w)}

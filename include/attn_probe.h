@@ -1,11 +1,16 @@
 /*
- * attn_probe.h - matrix-core rate probe of the MI355X (gfx950) attention library (libsdpa02.so).
+ * attn_probe.h - measurement probes of the MI355X (gfx950) attention library (libsdpa02.so).
  *
- * A measurement aid, not part of the attention computation. The attention entry points (attn.h) run
- * their QK^T and PV contractions and the backward's products on the matrix cores; their throughput is
- * reported as a fraction of the chip's published dense bf16 peak. This probe measures, on the same
- * device and in the same process, the rate the matrix cores sustain from registers alone and the engine
- * clock they run at, as a ceiling to read those fractions against.
+ * Measurement aids, not part of the attention computation.
+ *  - attn_mfma_probe: the attention entry points (attn.h) run their QK^T and PV contractions and the
+ *    backward's products on the matrix cores, and their throughput is reported as a fraction of the
+ *    chip's published dense bf16 peak. This probe measures, on the same device and in the same
+ *    process, the rate the matrix cores sustain from registers alone and the engine clock they run at,
+ *    as a ceiling to read those fractions against.
+ *  - attn_lds_probe: the kernels stage K/V (forward, dQ pass) and Q/dO (dK/dV pass) tiles in LDS and
+ *    read them back as matrix-core operands; how the LDS serves a read (its banks, and which lanes share
+ *    a cycle) decides the tile swizzle. This probe issues one wave's reads at caller-chosen per-lane
+ *    addresses, to be run under the SQ_LDS_BANK_CONFLICT counter.
  */
 #ifndef SDPA02_ATTN_PROBE_H
 #define SDPA02_ATTN_PROBE_H
@@ -37,6 +42,27 @@ extern "C" {
 #define ATTN_PROBE_MAX_ITERS (1 << 24)
 attn_status_t attn_mfma_probe(int32_t blocks, int32_t iters, float x, float y, float* out, size_t out_bytes,
                               uint64_t* ticks, size_t ticks_bytes, void* stream);
+
+/* Launches one wave (a workgroup of 64 threads) on `stream`. The wave fills an LDS array of
+ * ATTN_LDS_PROBE_BYTES bytes, then every lane l with lane_addr[l] >= 0 reads at byte address
+ * lane_addr[l] of it, 8 * iters times (lanes with a negative entry stay inactive):
+ *   kind ATTN_LDS_READ_B128 (0): ds_read_b128, 16 bytes; ATTN_LDS_READ_B64_TR_B16 (1): the transpose read
+ *   ds_read_b64_tr_b16, 8 bytes; ATTN_LDS_READ_B64 (2): ds_read_b64, 8 bytes.
+ * So the dispatch issues 8 * iters reads of that kind (plus the fill's ATTN_LDS_PROBE_BYTES / 1024
+ * ds_write_b128), and SQ_LDS_BANK_CONFLICT / (8 * iters) is the extra cycles per read.
+ *   lane_addr  host int32[64]: every non-negative entry a multiple of the read's width (16 or 8) with
+ *              entry + width <= ATTN_LDS_PROBE_BYTES;
+ *   out        device int32[64] (out_bytes at least 256): lane l writes the sum of what it read.
+ * iters in [1, ATTN_LDS_PROBE_MAX_ITERS]. Otherwise nothing is launched and the status says why
+ * (ATTN_E_INVALID / ATTN_E_ALIGN / ATTN_E_WORKSPACE). Asynchronous on `stream`; lane_addr is read
+ * before the call returns. */
+#define ATTN_LDS_PROBE_BYTES 32768
+#define ATTN_LDS_PROBE_MAX_ITERS (1 << 20)
+#define ATTN_LDS_READ_B128 0
+#define ATTN_LDS_READ_B64_TR_B16 1
+#define ATTN_LDS_READ_B64 2
+attn_status_t attn_lds_probe(int32_t kind, const int32_t* lane_addr, int32_t iters, int32_t* out, size_t out_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }

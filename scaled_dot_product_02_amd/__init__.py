@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     attn_fwd_workspace_bytes,
     attn_merge,
     attn_mfma_probe,
+    attn_lds_probe,
     lib,
     library_path,
     make_problem,

@@ -20,7 +20,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess",
-            "attn_bwd_noalloc", "attn_merge", "attn_mfma_probe",
+            "attn_bwd_noalloc", "attn_merge", "attn_mfma_probe", "attn_lds_probe",
             "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
             "attn_abi_version")
 MERGE_MAX_PARTS = 8
@@ -93,6 +93,8 @@ def lib():
         L.attn_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, vp, sz, vp, sz,
                                       vp]
         L.attn_mfma_probe.restype = ctypes.c_int
+        L.attn_lds_probe.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, sz, vp]
+        L.attn_lds_probe.restype = ctypes.c_int
         L.attn_fwd_workspace_bytes.argtypes = [pp]
         L.attn_fwd_workspace_bytes.restype = sz
         L.attn_bwd_workspace_bytes.argtypes = [pp]
@@ -432,6 +434,23 @@ def attn_merge(o_parts, lse_parts, cu_seqlens_q=None, max_seqlen_q=None, out=Non
     if st != 0:
         _raise(st)
     return out, lse
+
+
+LDS_READ_KINDS = {"b128": 0, "b64_tr_b16": 1, "b64": 2}  # ATTN_LDS_READ_*
+LDS_PROBE_BYTES = 32768  # ATTN_LDS_PROBE_BYTES
+
+
+def attn_lds_probe(kind, lane_addr, iters, out, stream=None):
+    """LDS read probe (attn_lds_probe): one wave reads 8 * iters times at lane_addr[l] (64 byte addresses,
+    negative = lane inactive) with the read `kind` ("b128", "b64_tr_b16", "b64"); `out` is a device int32
+    tensor of at least 64 elements. Asynchronous on `stream`."""
+    if len(lane_addr) != 64:
+        raise ValueError("lane_addr needs 64 entries")
+    arr = (ctypes.c_int32 * 64)(*[int(a) for a in lane_addr])
+    st = lib().attn_lds_probe(LDS_READ_KINDS[kind], arr, int(iters), _ptr(out), out.numel() * out.element_size(),
+                              _stream(stream))
+    if st != 0:
+        _raise(st)
 
 
 def attn_mfma_probe(blocks, iters, x=0.5, y=1.0 / 512, device="cuda:0", stream=None):

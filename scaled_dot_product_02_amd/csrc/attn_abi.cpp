@@ -558,4 +558,29 @@ attn_status_t attn_mfma_probe(int32_t blocks, int32_t iters, float x, float y, f
   }
 }
 
+attn_status_t attn_lds_probe(int32_t kind, const int32_t* lane_addr, int32_t iters, int32_t* out, size_t out_bytes,
+                             void* stream) {
+  try {
+    if (kind < ATTN_LDS_READ_B128 || kind > ATTN_LDS_READ_B64) return fail(ATTN_E_INVALID, "unknown read kind %d", kind);
+    if (iters < 1 || iters > ATTN_LDS_PROBE_MAX_ITERS)
+      return fail(ATTN_E_INVALID, "iters %d is not in [1, %d]", iters, ATTN_LDS_PROBE_MAX_ITERS);
+    if (!lane_addr || !out) return fail(ATTN_E_INVALID, "lane_addr or out is NULL");
+    if (!aligned(out, 4)) return fail(ATTN_E_ALIGN, "out is not 4-byte aligned");
+    if (out_bytes < 64 * sizeof(int32_t)) return fail(ATTN_E_WORKSPACE, "out holds %zu bytes, 256 needed", out_bytes);
+    const int width = kind == ATTN_LDS_READ_B128 ? 16 : 8;
+    for (int l = 0; l < 64; ++l) {
+      const int32_t x = lane_addr[l];
+      if (x < 0) continue;
+      if (x % width) return fail(ATTN_E_ALIGN, "lane %d address %d is not a multiple of %d", l, x, width);
+      if (x > ATTN_LDS_PROBE_BYTES - width)
+        return fail(ATTN_E_INVALID, "lane %d address %d: the read passes the %d-byte array", l, x, ATTN_LDS_PROBE_BYTES);
+    }
+    const int e = sdpa::launch_lds_probe(kind, lane_addr, iters, out, stream);
+    if (e) return fail(ATTN_E_HIP, "probe launch: %s", hipGetErrorString((hipError_t)e));
+    return ATTN_OK;
+  } catch (...) {
+    return fail(ATTN_E_INVALID, "internal error");
+  }
+}
+
 }  // extern "C"

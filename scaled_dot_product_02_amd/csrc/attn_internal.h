@@ -88,6 +88,7 @@ enum { kPassPre = 1, kPassDkdv = 2, kPassDq = 4, kPassDqPre = 8, kPassAll = 7 };
 int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stream);
 int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
 // Matrix-core rate probe (attn_probe.hip): blocks x 256 threads, iters rounds of four MFMAs per wave.
+int launch_lds_probe(int kind, const int32_t* lane_addr, int iters, int32_t* out, void* stream);
 int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsigned long long* ticks,
                       void* stream);
 int fwd_query_tile(int head_dim);

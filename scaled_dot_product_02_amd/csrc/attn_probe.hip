@@ -1,7 +1,10 @@
-// attn_probe.hip - a measurement aid beside the attention kernels: the matrix-core rate the device
-// sustains under a load of MFMA instructions alone, and its engine clock meanwhile. The attention
-// kernels do not use it; it gives their fraction-of-peak figures a measured ceiling next to the
-// published one.
+// attn_probe.hip - measurement aids beside the attention kernels, which do not use them:
+//  - the matrix-core rate the device sustains under a load of MFMA instructions alone, and its engine
+//    clock meanwhile (a measured ceiling next to the published peak for the fraction-of-peak figures);
+//  - an LDS read probe: one wave reading caller-chosen per-lane addresses, run under the bank-conflict
+//    counter to find how the LDS serves each read width (the basis of the tile swizzle in
+//    attn_device.h).
+#include "../../include/attn_probe.h"
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -9,6 +12,9 @@ namespace sdpa {
 namespace {
 
 constexpr int kProbeChains = 4;  // independent accumulator chains per wave
+constexpr int kLdsProbeBytes = ATTN_LDS_PROBE_BYTES;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Every wave runs `iters` rounds of kProbeChains independent 32x32x16 bf16 MFMAs on operands held in
 // registers: no memory traffic and no other instruction inside the loop. Lane l's operands are
@@ -50,7 +56,54 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(float x, float y, int i
   }
 }
 
+// One wave: the LDS array is filled, then every lane whose address is not negative reads 16 (kind 0,
+// ds_read_b128), 8 (kind 1, ds_read_b64_tr_b16) or 8 (kind 2, ds_read_b64) bytes at it, 8 times per
+// iteration; the address passes through an empty asm statement before each read so no read is merged
+// with another. Lane l writes the sum of what it read to out[l].
+struct LdsProbeArgs {
+  int32_t addr[64];
+};
+template <int KIND>
+__global__ void __launch_bounds__(64) lds_probe_kernel(LdsProbeArgs a, int iters, int32_t* out) {
+  __shared__ __attribute__((aligned(1024))) char buf[kLdsProbeBytes];
+  for (int i = threadIdx.x; i < kLdsProbeBytes / 16; i += 64)
+    reinterpret_cast<v4i*>(buf)[i] = v4i{i, 3 * i, 5 * i, 7 * i};
+  __syncthreads();
+  const int x0 = a.addr[threadIdx.x];
+  int acc = 0;
+  if (x0 >= 0) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int x = x0;
+        asm volatile("" : "+v"(x));
+        if constexpr (KIND == 0) {
+          const v4i v = *reinterpret_cast<const v4i*>(buf + x);
+          acc += v[0] + v[3];
+        } else if constexpr (KIND == 1) {
+          const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(buf + x));
+          acc += v[0] + v[3];
+        } else {
+          const v2i v = *reinterpret_cast<const v2i*>(buf + x);
+          acc += v[0] + v[1];
+        }
+      }
+    }
+  }
+  out[threadIdx.x] = acc;
+}
+
 }  // namespace
+
+int launch_lds_probe(int kind, const int32_t* lane_addr, int iters, int32_t* out, void* stream) {
+  LdsProbeArgs a;
+  for (int l = 0; l < 64; ++l) a.addr[l] = lane_addr[l];
+  const hipStream_t st = (hipStream_t)stream;
+  if (kind == 0) hipLaunchKernelGGL(lds_probe_kernel<0>, dim3(1), dim3(64), 0, st, a, iters, out);
+  else if (kind == 1) hipLaunchKernelGGL(lds_probe_kernel<1>, dim3(1), dim3(64), 0, st, a, iters, out);
+  else hipLaunchKernelGGL(lds_probe_kernel<2>, dim3(1), dim3(64), 0, st, a, iters, out);
+  return (int)hipGetLastError();
+}
 
 int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsigned long long* ticks,
                       void* stream) {

@@ -376,6 +376,29 @@ def test_mfma_probe_declines(L):
         assert frag in L.attn_last_error().decode(), (kw, L.attn_last_error())
 
 
+def test_lds_probe_declines(L):
+    """The LDS read probe validates its kind, iteration count, buffers and every lane address on the host
+    before launching (no GPU needed for these)."""
+    out = 1 << 20  # fake aligned device address, never dereferenced
+
+    def call(kind=0, addrs=None, iters=4, o=out, ob=256):
+        arr = (ctypes.c_int32 * 64)(*(addrs if addrs is not None else [16 * l for l in range(64)]))
+        return L.attn_lds_probe(kind, arr, iters, o, ob, None)
+
+    lane5 = lambda a: [a if l == 5 else -1 for l in range(64)]
+    cases = [
+        (dict(kind=3), INVALID, "kind"), (dict(kind=-1), INVALID, "kind"),
+        (dict(iters=0), INVALID, "iters"), (dict(iters=(1 << 20) + 1), INVALID, "iters"),
+        (dict(o=None), INVALID, "NULL"), (dict(o=out + 2), ALIGN, "out"), (dict(ob=252), WORKSPACE, "out holds"),
+        (dict(addrs=lane5(8)), ALIGN, "lane 5"), (dict(kind=1, addrs=lane5(4)), ALIGN, "lane 5"),
+        (dict(addrs=lane5(32768 - 8)), ALIGN, "lane 5"), (dict(addrs=lane5(32768)), INVALID, "passes"),
+        (dict(kind=2, addrs=lane5(32768 - 4)), ALIGN, "lane 5"), (dict(kind=2, addrs=lane5(32768)), INVALID, "passes"),
+    ]
+    for kw, want, frag in cases:
+        assert call(**kw) == want, kw
+        assert frag in L.attn_last_error().decode(), (kw, L.attn_last_error())
+
+
 @pytest.mark.parametrize("entry", sorted(set(B.BWD_PASSES.values())))
 def test_every_backward_entry_point_validates(L, entry):
     """Each backward entry point (attn_bwd and the single passes, the fused dQ + preprocess pass

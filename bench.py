@@ -50,9 +50,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "b3c9c7a7946c", "bytes": 874901969},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "904f89aa94fc", "bytes": 933682204},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "8b13bc8d8996", "bytes": 698814589},
+    ("dense_d128", "fwd"): {"fingerprint": "65fb8f54832c", "bytes": 861961075},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "618b28ad1145", "bytes": 1005566012},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "1773d3abeba9", "bytes": 699838454},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 

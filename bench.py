@@ -50,9 +50,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "65fb8f54832c", "bytes": 861961075},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "618b28ad1145", "bytes": 1005566012},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "1773d3abeba9", "bytes": 699838454},
+    ("dense_d128", "fwd"): {"fingerprint": "1150214bcc3c", "bytes": 874132512},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "b70010ae45e0", "bytes": 1019066078},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "42c38569a687", "bytes": 745611825},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
@@ -258,7 +258,7 @@ def atomic_supported(w):
     return max(w.d, w.d_v) <= 128
 
 
-def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False):
+def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False, exp_split=False):
     """Time `steps` steps of workload w. With flush_mall, a 512 MiB buffer is overwritten before every
     timed step (outside the per-kernel events), so no input is still in the 256 MB memory-side cache
     when a step starts; ms_step then includes the fill and only the per-kernel times are meaningful."""
@@ -298,7 +298,8 @@ def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, **{n: a for n, a in kw.items() if n != "atomic_dq"})
+        sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, exp_split=exp_split,
+                    **{n: a for n, a in kw.items() if n != "atomic_dq"})
         for i, pas in enumerate(seq):
             mark(1 + i)
             sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=(pas,), **kw)
@@ -528,6 +529,20 @@ def single_pass_measure(w, steps, warmup):
                                 for n, e in kroof.items()}}
 
 
+def exp_split_measure(w, steps, warmup):
+    """The same workload with the forward's exp split (ATTN_FLAG_FWD_EXP_SPLIT: a quarter of the exponentials
+    on interior tiles by a VALU polynomial), the default backward: forward ms and TFLOP/s."""
+    r = run(w, steps, warmup, exp_split=True)
+    fp = flop_per_pair(w)
+    km = r["kern_ms"]
+    f_fwd = fp["fwd"] * r["pairs"]
+    return {"what": "forward with ATTN_FLAG_FWD_EXP_SPLIT (one in four exponentials of each lane on interior tiles "
+                    "by a degree-5 polynomial on the VALU), default backward",
+            "fwd": {"ms": round(km["fwd"], 4), "tflops": round(f_fwd / (km["fwd"] * 1e-3) / 1e12, 2),
+                    "frac_of_peak": round(f_fwd / (km["fwd"] * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},
+            "ms_per_step": round(r["ms_step"], 4)}
+
+
 # The named cases timed in every default run besides the headline (dense_d128): the tiny case, the packed
 # GQA batch, the D=512 layer and the two single-rank context-parallel shares.
 CASES = ("tiny", "thd_d128", "dense_d512", "cp_share_d256", "cp_share_d512")
@@ -626,6 +641,8 @@ def main():
     if not args.no_extra and atomic_supported(w):
         log("single-pass backward on the same workload")
         out["single_pass"] = single_pass_measure(w, args.steps, args.warmup)
+        if max(w.d, w.d_v) <= 256:  # the exp split is built for head dims up to 256
+            out["exp_split"] = exp_split_measure(w, max(5, args.steps // 2), 3)
     if not args.no_extra and w.name == "dense_d128":
         out["cases"] = {}
         for name in CASES:

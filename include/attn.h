@@ -134,6 +134,17 @@ typedef struct attn_problem {
  * attn_bwd_dq_preprocess is ATTN_E_UNSUPPORTED. */
 #define ATTN_FLAG_BWD_ATOMIC_DQ 1
 
+/* Exp split in the forward (pull request 3705, section Follow-up causal THD forward kernel optimization:
+ * a quarter of the softmax exponentials on interior tiles moved from the transcendental unit to an FMA
+ * implementation). With the flag, on every key tile that needs no mask one in four of each lane's
+ * exponentials is computed as 2^n * p(x - n), n = rint(x), p a degree-5 polynomial (Cody-Waite reduction,
+ * relative error below 2.0e-7, the transcendental unit's is about the same), the others by the unit.
+ * Results agree with the default forward to fp32 rounding of P, not bit for bit. Head dims up to 256
+ * (both head_dim and head_dim_v); wider heads are ATTN_E_UNSUPPORTED. Measured slower on gfx950 (its
+ * exponential unit overlaps the VALU and is not the limit), so off by default. The backward ignores the
+ * flag. */
+#define ATTN_FLAG_FWD_EXP_SPLIT 2
+
 /* Workspace (pull request 3705, section Execution and supported scope: the caller binds the workspace
  * on every call; pull request 3527, section Known limitations: the backward workspace there grows
  * super-linearly, here it is linear in tokens). Its first 256 bytes are a header whose int32 at

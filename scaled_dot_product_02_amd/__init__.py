@@ -10,6 +10,7 @@ combines forward results over disjoint key chunks (the ring context-parallel ste
 from ._binding import (  # noqa: F401
     ABI_VERSION,
     FLAG_BWD_ATOMIC_DQ,
+    FLAG_FWD_EXP_SPLIT,
     AttnError,
     AttnProblem,
     attn_bwd,

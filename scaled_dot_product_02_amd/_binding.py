@@ -16,6 +16,7 @@ LIB_NAME = "libsdpa02.so"
 
 ABI_VERSION = 4
 FLAG_BWD_ATOMIC_DQ = 1  # ATTN_FLAG_BWD_ATOMIC_DQ
+FLAG_FWD_EXP_SPLIT = 2  # ATTN_FLAG_FWD_EXP_SPLIT
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
@@ -267,12 +268,13 @@ def attn_bwd_workspace_bytes(p):
 
 
 def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None, max_seqlen_q=None,
-             max_seqlen_kv=None, out=None, lse=None, workspace=None, stream=None, window_left=-1):
+             max_seqlen_kv=None, out=None, lse=None, workspace=None, stream=None, window_left=-1, exp_split=False):
     """Forward through the C-ABI. Returns (O, LSE).
 
     Dense q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D]; packed q [Tq,Hq,D], k/v [Tkv,Hkv,D] with int32
     cu_seqlens on the device. V (and O) may have their own head dim D_v; O is then [..., Hq, D_v].
-    LSE is fp32 [B,Hq,Sq] (dense) or [Tq,Hq] (packed).
+    LSE is fp32 [B,Hq,Sq] (dense) or [Tq,Hq] (packed). ``exp_split`` sets ATTN_FLAG_FWD_EXP_SPLIT (a quarter
+    of the exponentials on interior tiles by a VALU polynomial; head dims up to 256).
     """
     import torch
     packed = cu_seqlens_q is not None
@@ -283,7 +285,7 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
         shape = (q.shape[0], q.shape[1]) if packed else (q.shape[0], q.shape[2], q.shape[1])
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     p = make_problem(q, k, v, out, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                     window_left)
+                     window_left, FLAG_FWD_EXP_SPLIT if exp_split else 0)
     L = lib()
     need = L.attn_fwd_workspace_bytes(ctypes.byref(p))
     ws = _workspace(need, q.device, workspace)

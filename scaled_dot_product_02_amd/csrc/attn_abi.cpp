@@ -108,7 +108,8 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (!(p->scale > 0.f)) return fail(ATTN_E_UNSUPPORTED, "scale %g is not positive", (double)p->scale);
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
   if (p->window_left < -1) return fail(ATTN_E_INVALID, "window_left %d < -1", p->window_left);
-  if (p->flags & ~ATTN_FLAG_BWD_ATOMIC_DQ) return fail(ATTN_E_INVALID, "unknown flags 0x%x", (unsigned)p->flags);
+  if (p->flags & ~(ATTN_FLAG_BWD_ATOMIC_DQ | ATTN_FLAG_FWD_EXP_SPLIT))
+    return fail(ATTN_E_INVALID, "unknown flags 0x%x", (unsigned)p->flags);
   if (p->window_left >= 0 && p->mask == ATTN_MASK_NONE)
     return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
                 p->window_left);
@@ -277,6 +278,9 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
     attn_status_t st = check_problem(p, &in);
     if (st != ATTN_OK) return st;
     const int dqk = p->head_dim, dv = head_dim_v(p);
+    if ((p->flags & ATTN_FLAG_FWD_EXP_SPLIT) && sdpa::instance_head_dim(dqk, dv) > 256)
+      return fail(ATTN_E_UNSUPPORTED, "the exp split (ATTN_FLAG_FWD_EXP_SPLIT) is built for head dims up to 256, "
+                                      "not %d/%d", dqk, dv);
     const Extent eq = ext_q(p, q, p->q_stride, false, in, dqk), ek = ext_q(p, k, p->k_stride, true, in, dqk),
                  ev = ext_q(p, v, p->v_stride, true, in, dv), eo = ext_q(p, o, p->o_stride, false, in, dv),
                  el = ext_lse(p, lse, in);
@@ -304,6 +308,7 @@ attn_status_t attn_fwd(const attn_problem_t* p, const void* q, const void* k, co
       return fail(ATTN_E_OVERLAP, "workspace overlaps a tensor");
     sdpa::FwdArgs a{};
     const int inst = sdpa::instance_head_dim(dqk, dv);
+    a.exp_split = (p->flags & ATTN_FLAG_FWD_EXP_SPLIT) != 0;
     a.s = make_shape(p, in, ws, sdpa::fwd_query_tile(inst));
     if (in.packed) {  // every packed call rewrites the error word from its own offsets
       const int e = sdpa::launch_validate_cu(a.s, stream);

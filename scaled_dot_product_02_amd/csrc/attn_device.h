@@ -168,6 +168,24 @@ __device__ __forceinline__ int opaque(int x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the VALU (the forward's optional exp split): Cody-Waite reduction specialised to base 2, which is
+// exact in fp32 (n = rint(x), f = x - n in [-1/2, 1/2]), a degree-5 polynomial for 2^f, then v_ldexp_f32.
+// The coefficients are the float32-rounded least-squares fit of the relative error made by
+// scaled_dot_product_02_amd/exp2_poly.py (max relative error 2.0e-7 for x in [-30, 8]; a CPU test holds
+// these literals to that fit). x is clamped at -127: 2^-127 is far below anything a row sum can see.
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -127.f);
+  const float n = __builtin_rintf(x);
+  const float f = x - n;
+  float p = 1.326697064e-03f;
+  p = __builtin_fmaf(p, f, 9.675459936e-03f);
+  p = __builtin_fmaf(p, f, 5.550742522e-02f);
+  p = __builtin_fmaf(p, f, 2.402212173e-01f);
+  p = __builtin_fmaf(p, f, 6.931469440e-01f);
+  p = __builtin_fmaf(p, f, 1.000000119e+00f);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Reductions over the lane pair (l, l ^ 32) with v_permlane32_swap (no LDS round trip): the swap

@@ -38,6 +38,7 @@ struct FwdArgs {
   float* lse;
   TensorAddr aq, ak, av, ao;
   TensorAddr alse;  // LSE addressing (d term absent)
+  int32_t exp_split;  // ATTN_FLAG_FWD_EXP_SPLIT: a quarter of the interior tiles' exponentials on the VALU
 };
 
 struct BwdArgs {

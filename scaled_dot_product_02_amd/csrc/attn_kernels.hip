@@ -242,7 +242,9 @@ __global__ void __launch_bounds__(256) validate_cu_kernel(AttnShape s) {
 // ------------------------------------------------------------------------------------------
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int D, int BN, int MINW, typename T, bool PAD>
+// EXPS: the optional exp split (ATTN_FLAG_FWD_EXP_SPLIT), one in four of each lane's exponentials on tiles
+// without a mask computed by exp2_poly.
+template <int D, int BN, int MINW, typename T, bool PAD, bool EXPS = false>
 __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   constexpr int BM = 128;
   constexpr int CH = D / 8;
@@ -380,14 +382,26 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
     }
     const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;  // rows with no key yet: every P is 0
+    if (EXPS && !need_mask) {  // exp split: one in four of the lane's exponentials on the VALU
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int jr = 0; jr < 16; ++jr) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[kb][jr], c, -m_use));
-        sacc[kb][jr] = p;
-        l_run += p;
-      }
+        for (int jr = 0; jr < 16; ++jr) {
+          const float x = __builtin_fmaf(sacc[kb][jr], c, -m_use);
+          const float p = (jr & 3) == 3 ? exp2_poly(x) : fast_exp2(x);
+          sacc[kb][jr] = p;
+          l_run += p;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int jr = 0; jr < 16; ++jr) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[kb][jr], c, -m_use));
+          sacc[kb][jr] = p;
+          l_run += p;
+        }
+    }
     // O^T += V^T P^T, 16 keys per MFMA: k-chunk cp of block kb takes S^T registers 4cp..4cp+3 and
     // 8+4cp..8+4cp+3, i.e. keys 32kb + 8cp + 4hh + 0..3 and the same + 16
 #pragma unroll
@@ -1918,7 +1932,10 @@ static int fwd_t(const FwdArgs& a, hipStream_t st) {
   // 32-key tiles (253 registers, no spills); measured 35 % faster than the split kernel's wave pairs
   // (cp_share_d256 1.45 -> 0.94 ms, window_d256 0.295 -> 0.191 ms, asym_d192 1.43 -> 0.93 ms)
   if constexpr (D <= 256) {
-    hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
+    if (a.exp_split)
+      hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T, PAD, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<D, fwd_bn<D>(), fwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL((attn_fwd_split_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
   }

@@ -64,7 +64,7 @@ def _nan_like(shape, dtype, dev):
     return torch.full(shape, float("nan"), dtype=dtype, device=dev)
 
 
-def gpu_run(w, x, backward=True, stream=None, atomic_dq=False):
+def gpu_run(w, x, backward=True, stream=None, atomic_dq=False, exp_split=False):
     """Forward (and backward) of workload w on cuda:0 through the C-ABI; returns CPU tensors.
 
     Every output buffer starts as NaN, so an element that no kernel writes (or that a kernel writes
@@ -78,7 +78,7 @@ def gpu_run(w, x, backward=True, stream=None, atomic_dq=False):
     o = _nan_like(q.shape[:-1] + v.shape[-1:], q.dtype, dev)
     lse_shape = (q.shape[0], q.shape[1]) if w.packed else (q.shape[0], q.shape[2], q.shape[1])
     lse = _nan_like(lse_shape, torch.float32, dev)
-    o, lse = sd.attn_fwd(q, k, v, out=o, lse=lse, stream=stream, **kw)
+    o, lse = sd.attn_fwd(q, k, v, out=o, lse=lse, stream=stream, exp_split=exp_split, **kw)
     out = dict(o=o, lse=lse)
     if backward:
         do = x["do"].to(dev)
@@ -223,8 +223,8 @@ def all_units(w, x):
     return [(b, g) for b in range(nseq) for g in range(w.hkv)]
 
 
-def run_and_check(w, units=None, backward=True, atomic_dq=False):
+def run_and_check(w, units=None, backward=True, atomic_dq=False, exp_split=False):
     x = make_inputs(w)
-    got = gpu_run(w, x, backward=backward, atomic_dq=atomic_dq)
+    got = gpu_run(w, x, backward=backward, atomic_dq=atomic_dq, exp_split=exp_split)
     assert_all_written(w.name, got)
     return check_units(w, x, got, units if units is not None else all_units(w, x))

@@ -439,7 +439,7 @@ def test_single_pass_backward_flag(L):
     and q-head to the backward workspace; head dims past 128 and the fused dQ + preprocess pass are
     declined with a reason, before any launch."""
     p = dense_problem()
-    p.flags = 2
+    p.flags = 4
     expect(L, bwd(L, p), INVALID, "unknown flags")
     p = dense_problem(b=2, sq=256, hq=4, d=128)
     base = L.attn_bwd_workspace_bytes(ctypes.byref(p))
@@ -452,3 +452,20 @@ def test_single_pass_backward_flag(L):
     expect(L, bwd(L, wide), UNSUPPORTED, "head dims up to 128")
     need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
     expect(L, bwd(L, p, ws_bytes=need - 256), WORKSPACE, "workspace")
+
+
+def test_exp_split_flag(L):
+    """ATTN_FLAG_FWD_EXP_SPLIT: the forward declines it past head dim 256 with a reason before any launch;
+    it changes no workspace size."""
+    for d, dv in ((512, 0), (64, 512), (512, 128)):
+        p = dense_problem(d=d)
+        p.head_dim_v = dv
+        p.flags = B.FLAG_FWD_EXP_SPLIT
+        expect(L, fwd(L, p), UNSUPPORTED, "head dims up to 256")
+    p = dense_problem(b=2, sq=256, hq=4, d=128)
+    base_f, base_b = L.attn_fwd_workspace_bytes(ctypes.byref(p)), L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    p.flags = B.FLAG_FWD_EXP_SPLIT
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(p)) == base_f
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(p)) == base_b
+    p.flags = B.FLAG_FWD_EXP_SPLIT | 4
+    expect(L, fwd(L, p), INVALID, "unknown flags")

@@ -1001,10 +1001,12 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     dma.copy(kg + (int64_t)kv0 * a.ak.row, vg + (int64_t)kv0 * a.av.row, sq.skv - 1 - kv0, ks, vs);
   };
 
-  // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
-  // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
+  // K/V rows 16m + l16, chunk 4kk + G -> element rrow + 16m*D + ((32kk) ^ rkey); transpose reads: rows
+  // 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tkey) (lane chunk bits folded into the keys). The
+  // reads below take these in bytes from a per-half base, one XOR each (see there).
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
+  static_assert(((2 * KTILE) & (D - 1)) == 0, "stage offsets must leave the chunk bits alone");
   if constexpr (PAD) {
     zero_lds<2 * 2 * KTILE>(smem);
     __syncthreads();
@@ -1016,9 +1018,10 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
 #pragma unroll
    for (int kh = 0; kh < KH; ++kh) {  // 32-key half of the tile
-    const int rx = opaque(rkey), tx = opaque(tkey);
-    const us* ks = smem + (j & 1) * 2 * KTILE + 32 * kh * D;
-    const us* vs = ks + KTILE;
+    // per-half byte bases: the stage, half and row parts never touch the swizzled chunk bits, so each
+    // read below is one XOR with a constant plus an immediate offset
+    const int hb = 4 * (j & 1) * KTILE + 64 * kh * D;
+    const int rb = opaque(2 * (rrow + rkey)) + hb, tb = opaque(2 * (trow + tkey)) + hb;
     const int kv0 = j * BK + 32 * kh;
     if (s.mask != 0 && kv0 > qw0 + QW - 1 + delta) continue;
     if (s.wl >= 0 && kv0 + 31 < qw0 + delta - s.wl) continue;  // keys before this wave's windows
@@ -1035,9 +1038,9 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const int o = rrow + 16 * kb * D + ((32 * kk) ^ rx);
-        const v8s ka = lds_read16(ks, o);
-        const v8s va = lds_read16(vs, o);
+        const int o = (rb ^ (64 * kk)) + 32 * kb * D;
+        const v8s ka = lds_read16_at(smem, o);
+        const v8s va = lds_read16_at(smem, o + 2 * KTILE);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           st[kb][qb] = Elem<T>::mma16(Elem<T>::cast(ka), Elem<T>::cast(qf[qb][kk]), st[kb][qb]);
@@ -1076,8 +1079,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = trow + ((16 * dt) ^ tx);
-      const v8s kbt = cat44(lds_read_tr(ks, o1), lds_read_tr(ks, o1 + 16 * D));
+      const int o1 = tb ^ (32 * dt);
+      const v8s kbt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) dq[qb][dt] = Elem<T>::mma16(dsa[qb], Elem<T>::cast(kbt), dq[qb][dt]);
     }

@@ -533,17 +533,19 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
-    const us* ks = smem + (j & 1) * 2 * TILE;
-    const us* vs = ks + TILE;
+    // per-stage byte bases: the stage, row and half-of-D parts never touch the bits the XOR constants
+    // below flip, so each read is one XOR plus an immediate offset
+    const int sbb = 4 * (j & 1) * TILE;
+    const int kb_ = opaque(2 * (krow + kkey)) + sbb;
+    const int vb0 = opaque(2 * (vrow + vkey[0])) + sbb + 2 * TILE, vb1 = opaque(2 * (vrow + 8 * D + vkey[1])) + sbb + 2 * TILE;
     const int kv0 = j * BN;
     const bool active = (s.mask == 0 || kv0 <= qw0 + 31 + delta) &&
                         (s.wl < 0 || kv0 + BN - 1 >= qw0 + delta - s.wl);  // same for both waves of a pair
-    const int kx = opaque(kkey), vx0 = opaque(vkey[0]), vx1 = opaque(vkey[1]);
     v16f sacc = v16f{};
     if (active && (!PAD || hf * DH < s.dqk)) {  // a half of D wholly past D_qk adds 0 to S
 #pragma unroll
       for (int kk = 0; kk < DH / 16; ++kk) {
-        const v8s kf = lds_read16(ks, krow + ((16 * kk) ^ kx));
+        const v8s kf = lds_read16_at(smem, kb_ ^ (32 * kk));
         sacc = Elem<T>::mma32(Elem<T>::cast(kf), Elem<T>::cast(qf[kk]), sacc);
       }
 #pragma unroll
@@ -606,12 +608,12 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
     for (int cp = 0; cp < 2; ++cp) {
       const auto pb = pack8<T>(sacc[4 * cp + 0], sacc[4 * cp + 1], sacc[4 * cp + 2], sacc[4 * cp + 3],
                                sacc[8 + 4 * cp + 0], sacc[8 + 4 * cp + 1], sacc[8 + 4 * cp + 2], sacc[8 + 4 * cp + 3]);
-      const int vx = cp ? vx1 : vx0;
+      const int vb = cp ? vb1 : vb0;
 #pragma unroll
       for (int dt = 0; dt < DH / 32; ++dt) {
-        const int o1 = vrow + 8 * cp * D + ((32 * dt) ^ vx);
-        const v4s lo = lds_read_tr(vs, o1);
-        const v4s hi = lds_read_tr(vs, o1 + 16 * D);
+        const int o1 = vb ^ (64 * dt);
+        const v4s lo = lds_read_tr_at(smem, o1);
+        const v4s hi = lds_read_tr_at(smem, o1 + 32 * D);
         oacc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), pb, oacc[dt]);
       }
     }
@@ -1120,7 +1122,10 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   constexpr int QTILE = BQ * D;
   constexpr int NDMA = QTILE * 2 / 1024 / NW;
   static_assert(NDMA >= 1, "query tile must split over 8 waves");
-  constexpr int STAGE = 2 * QTILE + 2 * 64 * 2;  // Q, dO tiles, then lse2[64] and D[64] as floats
+  // Q, dO tiles, then lse2[64] and D[64] as floats, padded so that a stage offset leaves the chunk bits
+  // of a row alone (the reads below XOR them into per-stage byte bases)
+  constexpr int STAGE = 2 * QTILE + D;
+  static_assert((STAGE & (D - 1)) == 0 && 2 * 64 * 2 <= D, "stage padding");
   __shared__ __attribute__((aligned(1024))) us smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float xch[4 * 2 * 64 * 4];  // P per pair: [qb][lane][4]
   const AttnShape& s = a.s;
@@ -1179,8 +1184,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     ld.next();
   };
 
-  // Q/dO (or K/V) rows 16m + l16, chunk 4kk + G -> rrow + 16m*D + ((32kk) ^ rx); transpose reads:
-  // rows 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tx) (lane chunk bits folded into the keys)
+  // Q/dO rows 16m + l16, chunk 4kk + G -> element rrow + 16m*D + ((32kk) ^ rkey); transpose reads: rows
+  // 4G + rr (+16), chunk 2dt + cc/2 -> trow + ((16dt) ^ tkey) (lane chunk bits folded into the keys). The
+  // reads take these in bytes from per-stage bases, one XOR each.
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   float* pbuf = xch + pr * 2 * 64 * 4;
@@ -1195,7 +1201,11 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_it) issue((it + 1) & 1);
-    const int rx = opaque(rkey), tx = opaque(tkey);
+    // per-stage byte bases of this wave's row reads (Q for role 0, dO for role 1) and transpose reads
+    // (dO for role 0, Q for role 1): one XOR with a constant per read, the rest in immediate offsets
+    const int sbb = 2 * (it & 1) * STAGE;
+    const int rb = opaque(2 * (rrow + rkey)) + sbb + (role == 0 ? 0 : 2 * QTILE);
+    const int tb = opaque(2 * (trow + tkey)) + sbb + (role == 0 ? 2 * QTILE : 0);
     const us* qs = smem + (it & 1) * STAGE;
     const us* dos = qs + QTILE;
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
@@ -1208,25 +1218,24 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
                            (s.wl >= 0 && qs0 + BQ - 1 + delta - s.wl > kw0);
     v4f sv[2];  // role 0: S then P; role 1: dP then dS
     if (active) {
-      const us* src = role == 0 ? qs : dos;
       // the two 16-row blocks alternate (two independent accumulator chains) and the Q / dO fragments
       // are read RA products ahead: the two waves of a SIMD move in step here and cannot hide each
       // other's LDS latency
       constexpr int NT = 2 * (D / 32), RA = 4;
-      v8s rb[RA];
+      v8s rbuf[RA];
 #pragma unroll
-      for (int i = 0; i < RA; ++i) rb[i] = lds_read16(src, rrow + 16 * (i & 1) * D + ((32 * (i >> 1)) ^ rx));
+      for (int i = 0; i < RA; ++i) rbuf[i] = lds_read16_at(smem, (rb ^ (64 * (i >> 1))) + 32 * (i & 1) * D);
       sv[0] = v4f{};
       sv[1] = v4f{};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const v8s x = rb[t % RA];
+        const v8s x = rbuf[t % RA];
         __builtin_amdgcn_sched_barrier(0);
         sv[t & 1] = Elem<T>::mma16(Elem<T>::cast(x), Elem<T>::cast(kvf[t >> 1]), sv[t & 1]);
         __builtin_amdgcn_sched_barrier(0);
         if (t + RA < NT) {
           const int u = t + RA;
-          rb[t % RA] = lds_read16(src, rrow + 16 * (u & 1) * D + ((32 * (u >> 1)) ^ rx));
+          rbuf[t % RA] = lds_read16_at(smem, (rb ^ (64 * (u >> 1))) + 32 * (u & 1) * D);
         }
       }
       if (role == 0) {
@@ -1264,11 +1273,11 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
       }
     }
     const auto pa = pack8<T>(sv[0][0], sv[0][1], sv[0][2], sv[0][3], sv[1][0], sv[1][1], sv[1][2], sv[1][3]);
-    const us* bsrc = role == 0 ? dos : qs;  // dV += P^T dO ; dK += dS^T Q
+    // dV += P^T dO ; dK += dS^T Q
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = trow + ((16 * dt) ^ tx);
-      const v8s bt = cat44(lds_read_tr(bsrc, o1), lds_read_tr(bsrc, o1 + 16 * D));
+      const int o1 = tb ^ (32 * dt);
+      const v8s bt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
       acc[dt] = Elem<T>::mma16(pa, Elem<T>::cast(bt), acc[dt]);
     }
   }
@@ -1368,22 +1377,21 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
-    const int rx = opaque(rkey), tx = opaque(tkey);
-    const us* ks = smem + (j & 1) * 2 * KTILE;
-    const us* vs = ks + KTILE;
+    // per-stage byte bases (K rows for role 0, V rows for role 1; K transposed for both): one XOR per read
+    const int sbb = 4 * (j & 1) * KTILE;
+    const int rb = opaque(2 * (rrow + rkey)) + sbb + (role == 0 ? 0 : 2 * KTILE), tb = opaque(2 * (trow + tkey)) + sbb;
     const int kv0 = j * BK;
     const bool active = (s.mask == 0 || kv0 <= qw0 + QW - 1 + delta) && (s.wl < 0 || kv0 + BK - 1 >= qw0 + delta - s.wl);
     const bool need_mask = (kv0 + BK > sq.skv) || (s.mask != 0 && kv0 + BK - 1 > qw0 + delta) ||
                            (s.wl >= 0 && kv0 < qw0 + QW - 1 + delta - s.wl);
     v4f st[2];  // S^T -> P (role 0) or dP^T (role 1): key kv0 + 16kb + 4G + i, query qw0 + l16
     if (active) {
-      const us* src = role == 0 ? ks : vs;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         st[kb] = v4f{};
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
-          st[kb] = Elem<T>::mma16(Elem<T>::cast(lds_read16(src, rrow + 16 * kb * D + ((32 * kk) ^ rx))),
+          st[kb] = Elem<T>::mma16(Elem<T>::cast(lds_read16_at(smem, (rb ^ (64 * kk)) + 32 * kb * D)),
                                   Elem<T>::cast(qdf[kk]), st[kb]);
       }
       if (role == 0) {
@@ -1422,8 +1430,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
     const auto dsa = pack8<T>(ds[0][0], ds[0][1], ds[0][2], ds[0][3], ds[1][0], ds[1][1], ds[1][2], ds[1][3]);
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
-      const int o1 = trow + ((16 * dt) ^ tx);
-      const v8s kbt = cat44(lds_read_tr(ks, o1), lds_read_tr(ks, o1 + 16 * D));
+      const int o1 = tb ^ (32 * dt);
+      const v8s kbt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
       dq[dt] = Elem<T>::mma16(dsa, Elem<T>::cast(kbt), dq[dt]);
     }
   }

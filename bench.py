@@ -50,9 +50,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "1150214bcc3c", "bytes": 874132512},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "b70010ae45e0", "bytes": 1019066078},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "42c38569a687", "bytes": 745611825},
+    ("dense_d128", "fwd"): {"fingerprint": "1150214bcc3c", "bytes": 879642205},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "9e8ccde69c68", "bytes": 996136395},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "e079a6a29599", "bytes": 700168831},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 

@@ -718,6 +718,8 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
   const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
+  kt = end_aligned(kt, a.n_kvtiles, sq.skv, BKV);
+  if (kt < 0) return;
   const int k0 = kt * BKV;
   if (k0 >= sq.skv) return;
   const int kw0 = k0 + w * KW;
@@ -1223,6 +1225,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
   const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
+  kt = end_aligned(kt, a.n_kvtiles, sq.skv, BKV);
+  if (kt < 0) return;
   const int k0 = kt * BKV;
   if (k0 >= sq.skv) return;
   const int kw0 = k0 + pr * KW;
@@ -1590,6 +1594,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_fused_kernel(BwdArgs a) {
   tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
   const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
+  kt = end_aligned(kt, a.n_kvtiles, sq.skv, BKV);
+  if (kt < 0) return;
   const int k0 = kt * BKV;
   if (k0 >= sq.skv) return;
   const int kw0 = k0 + pr * KW;

@@ -11,6 +11,8 @@
  *    read them back as matrix-core operands; how the LDS serves a read (its banks, and which lanes share
  *    a cycle) decides the tile swizzle. This probe issues one wave's reads at caller-chosen per-lane
  *    addresses, to be run under the SQ_LDS_BANK_CONFLICT counter.
+ *  - attn_tile_order_probe: the workgroup -> (unit, tile) order every kernel launch follows, evaluated
+ *    on the host, so that its coverage of every (unit, tile) pair can be checked without a GPU.
  */
 #ifndef SDPA02_ATTN_PROBE_H
 #define SDPA02_ATTN_PROBE_H
@@ -63,6 +65,20 @@ attn_status_t attn_mfma_probe(int32_t blocks, int32_t iters, float x, float y, f
 #define ATTN_LDS_READ_B64 2
 attn_status_t attn_lds_probe(int32_t kind, const int32_t* lane_addr, int32_t iters, int32_t* out, size_t out_bytes,
                              void* stream);
+
+/* Host only (no HIP call). Writes, for each workgroup index i in [0, units * tiles), the unit and the
+ * tile that workgroup i of a launch over `units` units of `tiles` tiles each is given: unit_out[i] and
+ * tile_out[i]. cluster = 1 is the order of the query-tile passes (forward, dQ pass), cluster = 0 the
+ * order of the key-tile passes (dK/dV pass, before its end-aligned shift of each unit's tiles);
+ * reverse = 1 numbers the tiles from the last (the causal passes run their longest tiles first).
+ * A unit of the query-tile passes is a (sequence, q-head) pair, of the key-tile passes a
+ * (sequence, kv-head) pair. Every (unit, tile) pair occurs exactly once.
+ * Arguments: units, tiles >= 1 with units * tiles <= ATTN_TILE_ORDER_PROBE_MAX; reverse, cluster 0 or 1;
+ * unit_out, tile_out caller-owned host arrays of n = units * tiles int32 each. Otherwise nothing is
+ * written and the status says why (ATTN_E_INVALID). */
+#define ATTN_TILE_ORDER_PROBE_MAX (1 << 24)
+attn_status_t attn_tile_order_probe(int32_t units, int32_t tiles, int32_t reverse, int32_t cluster, int32_t* unit_out,
+                                    int32_t* tile_out, size_t n);
 
 #ifdef __cplusplus
 }

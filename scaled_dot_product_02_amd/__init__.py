@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     attn_merge,
     attn_mfma_probe,
     attn_lds_probe,
+    attn_tile_order_probe,
     lib,
     library_path,
     make_problem,

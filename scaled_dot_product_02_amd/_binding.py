@@ -21,7 +21,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_dq_preprocess",
-            "attn_bwd_noalloc", "attn_merge", "attn_mfma_probe", "attn_lds_probe",
+            "attn_bwd_noalloc", "attn_merge", "attn_mfma_probe", "attn_lds_probe", "attn_tile_order_probe",
             "attn_fwd_workspace_bytes", "attn_bwd_workspace_bytes", "attn_status_str", "attn_last_error",
             "attn_abi_version")
 MERGE_MAX_PARTS = 8
@@ -96,6 +96,9 @@ def lib():
         L.attn_mfma_probe.restype = ctypes.c_int
         L.attn_lds_probe.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, sz, vp]
         L.attn_lds_probe.restype = ctypes.c_int
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.attn_tile_order_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i32p, i32p, sz]
+        L.attn_tile_order_probe.restype = ctypes.c_int
         L.attn_fwd_workspace_bytes.argtypes = [pp]
         L.attn_fwd_workspace_bytes.restype = sz
         L.attn_bwd_workspace_bytes.argtypes = [pp]
@@ -453,6 +456,19 @@ def attn_lds_probe(kind, lane_addr, iters, out, stream=None):
                               _stream(stream))
     if st != 0:
         _raise(st)
+
+
+def attn_tile_order_probe(units, tiles, reverse=False, cluster=True):
+    """The kernels' workgroup order (attn_tile_order_probe, evaluated on the host): two lists of
+    units * tiles ints, the unit and the tile of each workgroup index. cluster=True is the order of the
+    query-tile passes (forward, dQ pass), False that of the dK/dV pass."""
+    n = int(units) * int(tiles)
+    u = (ctypes.c_int32 * max(n, 1))()
+    t = (ctypes.c_int32 * max(n, 1))()
+    st = lib().attn_tile_order_probe(int(units), int(tiles), int(bool(reverse)), int(bool(cluster)), u, t, n)
+    if st != 0:
+        _raise(st)
+    return list(u)[:n], list(t)[:n]
 
 
 def attn_mfma_probe(blocks, iters, x=0.5, y=1.0 / 512, device="cuda:0", stream=None):

@@ -588,4 +588,16 @@ attn_status_t attn_lds_probe(int32_t kind, const int32_t* lane_addr, int32_t ite
   }
 }
 
+attn_status_t attn_tile_order_probe(int32_t units, int32_t tiles, int32_t reverse, int32_t cluster, int32_t* unit_out,
+                                    int32_t* tile_out, size_t n) {
+  if (units < 1 || tiles < 1 || (int64_t)units * tiles > ATTN_TILE_ORDER_PROBE_MAX)
+    return fail(ATTN_E_INVALID, "units %d x tiles %d is not in [1, %d]", units, tiles, ATTN_TILE_ORDER_PROBE_MAX);
+  if ((reverse != 0 && reverse != 1) || (cluster != 0 && cluster != 1))
+    return fail(ATTN_E_INVALID, "reverse and cluster must be 0 or 1");
+  if (!unit_out || !tile_out) return fail(ATTN_E_INVALID, "unit_out or tile_out is NULL");
+  if (n != (size_t)units * (size_t)tiles) return fail(ATTN_E_INVALID, "n = %zu, units x tiles = %lld", n, (long long)units * tiles);
+  for (int i = 0; i < units * tiles; ++i) sdpa::tile_map_host(i, units, tiles, reverse != 0, cluster != 0, unit_out + i, tile_out + i);
+  return ATTN_OK;
+}
+
 }  // extern "C"

@@ -212,13 +212,26 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // one engine; with packed sequences of unequal length one engine then gets several times the
 // average work (measured: the packed Hkv8 dK/dV pass ran at half the dense rate). Each tile row is
 // therefore rotated by 8 units: a unit keeps its XCD and its tiles cycle through the engines.
-// cluster: with few tiles per unit (short sequences) the order is unit-major inside each XCD instead:
-// workgroup i still runs on XCD i % 8, and that XCD's consecutive workgroups take the tiles of one
-// unit, so the K/V tiles that a unit's query tiles share are read from HBM once and then hit the
-// XCD's L2; tile-major order would start a unit's second tile only after every unit's first, long
-// after its K/V left the L2. Measured on B128 H16 S256 D128: forward -9 %, dQ pass -7 %; the dK/dV
-// pass (Q/dO shared by a unit's key tiles) ran 2.6 % slower that way and keeps tile-major order.
+// cluster (the query-tile passes: forward, dQ) changes the order when units is a multiple of 8, so that
+// a unit keeps one XCD and its tiles run close together in time there, sharing their K/V through that
+// XCD's L2:
+//  - few tiles per unit (short sequences): unit-major inside each XCD. Workgroup i still runs on XCD
+//    i % 8, and that XCD's consecutive workgroups take the tiles of one unit; tile-major order would
+//    start a unit's second tile only after every unit's first, long after its K/V left the L2.
+//    Measured on B128 H16 S256 D128: forward -9 %, dQ pass -7 %.
+//  - more than kUnitsInFlight units per XCD: the XCD's units are taken kUnitsInFlight at a time, and
+//    each such group runs tile-major (longest tile first, each tile row rotated by one unit across
+//    the shader engines). Plain tile-major order spreads every round over all of the XCD's units, so
+//    their K/V no longer fits the caches once an XCD holds many units; plain unit-major order runs
+//    all of one unit's tiles at once, which measured slower on few long units (dense B2 H16 S8192:
+//    forward +7 %). Measured against tile-major (same-run A/B): B8 H32 S4096 D128 forward -19 %, dQ
+//    pass -17 %; the packed batch of 16 sequences U{256..4096}, H32/8 forward -6 %; B4 H32/8 S8192
+//    dQ pass -4.5 %; groups of 2 or 8 units measured within 2 % of 4. With at most kUnitsInFlight
+//    units per XCD the order is tile-major as before.
+// The dK/dV pass (Q/dO shared by a unit's key tiles) ran 2.6 % slower unit-major on short sequences
+// and keeps tile-major order.
 constexpr int kFewTiles = 4;
+constexpr int kUnitsInFlight = 4;
 // Key-tile passes (dK/dV): round t of tile_order's order takes, for a unit whose sequence has ceil(len /
 // tile_len) key tiles, its tile t - (n_tiles - that count); negative = nothing to do in this round. Units are
 // thereby aligned at the ends of their sequences, so each round holds tiles at the same distance from their
@@ -228,18 +241,31 @@ constexpr int kFewTiles = 4;
 __device__ __forceinline__ int end_aligned(int t, int n_tiles, int len, int tile_len) {
   return t - (n_tiles - (len + tile_len - 1) / tile_len);
 }
-__device__ __forceinline__ void tile_order(int units, int tiles, bool reverse, int& unit, int& tile,
-                                           bool cluster = false) {
-  const int i = blockIdx.x;
-  if (cluster && tiles <= kFewTiles && units % 8 == 0) {
+// The (unit, tile) of workgroup i (0 <= i < units * tiles; a bijection onto units x tiles). Host and device:
+// the library's attn_tile_order_probe evaluates the same function on the host.
+__host__ __device__ __forceinline__ void tile_map(int i, int units, int tiles, bool reverse, bool cluster, int& unit,
+                                                  int& tile) {
+  if (cluster && units % 8 == 0 && tiles <= kFewTiles) {
     const int k = i / 8;
     unit = (k / tiles) * 8 + i % 8;
     tile = k % tiles;
+  } else if (cluster && units % 8 == 0 && units / 8 > kUnitsInFlight) {
+    const int k = i / 8;                               // position in XCD i % 8's sequence
+    const int c = k / (kUnitsInFlight * tiles);        // group of units
+    const int left = units / 8 - kUnitsInFlight * c;   // units of this XCD from group c on
+    const int cu = left < kUnitsInFlight ? left : kUnitsInFlight;
+    const int r = k - c * kUnitsInFlight * tiles;      // position in the group, tile-major
+    tile = r / cu;
+    unit = (kUnitsInFlight * c + (r + tile) % cu) * 8 + i % 8;
   } else {
     tile = i / units;
     unit = (i % units + 8 * (tile % units)) % units;
   }
   if (reverse) tile = tiles - 1 - tile;
+}
+__device__ __forceinline__ void tile_order(int units, int tiles, bool reverse, int& unit, int& tile,
+                                           bool cluster = false) {
+  tile_map(blockIdx.x, units, tiles, reverse, cluster, unit, tile);
 }
 // Query-side units (forward, dQ pass) are q-heads in (sequence, q-head) order, so consecutive
 // q-heads, including the heads of one GQA group, run on different XCDs. Measured on the packed

@@ -90,6 +90,8 @@ int launch_bwd(int dtype, int head_dim, const BwdArgs& a, int passes, void* stre
 int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
 // Matrix-core rate probe (attn_probe.hip): blocks x 256 threads, iters rounds of four MFMAs per wave.
 int launch_lds_probe(int kind, const int32_t* lane_addr, int iters, int32_t* out, void* stream);
+// attn_device.h's workgroup order, evaluated on the host (attn_tile_order_probe)
+void tile_map_host(int i, int units, int tiles, bool reverse, bool cluster, int* unit, int* tile);
 int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsigned long long* ticks,
                       void* stream);
 int fwd_query_tile(int head_dim);

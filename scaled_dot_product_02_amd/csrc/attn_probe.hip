@@ -3,7 +3,8 @@
 //    clock meanwhile (a measured ceiling next to the published peak for the fraction-of-peak figures);
 //  - an LDS read probe: one wave reading caller-chosen per-lane addresses, run under the bank-conflict
 //    counter to find how the LDS serves each read width (the basis of the tile swizzle in
-//    attn_device.h).
+//    attn_device.h);
+//  - the kernels' workgroup order (tile_map in attn_device.h) evaluated on the host.
 #include "../../include/attn_probe.h"
 #include "attn_device.h"
 #include "attn_internal.h"
@@ -110,6 +111,13 @@ int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsig
   hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, x, y, iters,
                      out, ticks);
   return (int)hipGetLastError();
+}
+
+void tile_map_host(int i, int units, int tiles, bool reverse, bool cluster, int* unit, int* tile) {
+  int u = 0, t = 0;
+  tile_map(i, units, tiles, reverse, cluster, u, t);
+  *unit = u;
+  *tile = t;
 }
 
 }  // namespace sdpa

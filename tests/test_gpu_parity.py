@@ -75,6 +75,23 @@ def test_packed_sweep(d, dtype, mask, lens):
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
 
 
+# Query-side launches with more than four units per XCD (a unit count that is a multiple of 8, above 32)
+# and more than four query tiles per unit take each XCD's units four at a time; these cases end on a
+# partial group (5, 9 and 6 units per XCD) and are compared whole against the oracle.
+GROUPED_CASES = [
+    dict(batch=5, hq=8, hkv=8, sq=640, skv=640, d=64, dtype="bf16", mask="causal_tl"),
+    dict(batch=3, hq=24, hkv=8, sq=600, skv=700, d=128, dtype="fp16", mask="causal_br"),
+    dict(hq=8, hkv=4, d=64, dtype="bf16", mask="causal_tl", seqlens=(700, 513, 640, 129, 900, 1)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROUPED_CASES)))
+def test_grouped_unit_order(case):
+    w = small(f"grouped_{case}", seed=31 + case, **GROUPED_CASES[case])
+    ok, msgs = run_and_check(w)
+    assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
+
+
 # Full-size workloads: sampled units (sequence, kv-head) that the oracle computes whole. For the dense
 # MHA workloads the unit index b * Hkv + g is also the query-side unit of the forward and the dQ pass;
 # the samples take one unit per residue modulo 8 and the last unit.

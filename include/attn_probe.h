@@ -68,16 +68,20 @@ attn_status_t attn_lds_probe(int32_t kind, const int32_t* lane_addr, int32_t ite
 
 /* Host only (no HIP call). Writes, for each workgroup index i in [0, units * tiles), the unit and the
  * tile that workgroup i of a launch over `units` units of `tiles` tiles each is given: unit_out[i] and
- * tile_out[i]. cluster = 1 is the order of the query-tile passes (forward, dQ pass), cluster = 0 the
- * order of the key-tile passes (dK/dV pass, before its end-aligned shift of each unit's tiles);
- * reverse = 1 numbers the tiles from the last (the causal passes run their longest tiles first).
- * A unit of the query-tile passes is a (sequence, q-head) pair, of the key-tile passes a
- * (sequence, kv-head) pair. Every (unit, tile) pair occurs exactly once.
- * Arguments: units, tiles >= 1 with units * tiles <= ATTN_TILE_ORDER_PROBE_MAX; reverse, cluster 0 or 1;
- * unit_out, tile_out caller-owned host arrays of n = units * tiles int32 each. Otherwise nothing is
- * written and the status says why (ATTN_E_INVALID). */
+ * tile_out[i]. order selects the launch: ATTN_ORDER_QUERY the query-tile passes (forward, dQ pass; a unit
+ * is a (sequence, q-head) pair), ATTN_ORDER_GROUPED the dK/dV passes of dense batches and
+ * ATTN_ORDER_TILE_MAJOR those of packed batches (a unit is a (sequence, kv-head) pair; the tile is the
+ * round before the end-aligned shift of each unit's key tiles); reverse = 1 numbers the tiles from the
+ * last (the causal query-tile passes run their longest tiles first). Every (unit, tile) pair occurs
+ * exactly once.
+ * Arguments: units, tiles >= 1 with units * tiles <= ATTN_TILE_ORDER_PROBE_MAX; reverse 0 or 1; order one
+ * of the three values; unit_out, tile_out caller-owned host arrays of n = units * tiles int32 each.
+ * Otherwise nothing is written and the status says why (ATTN_E_INVALID). */
+#define ATTN_ORDER_TILE_MAJOR 0
+#define ATTN_ORDER_QUERY 1
+#define ATTN_ORDER_GROUPED 2
 #define ATTN_TILE_ORDER_PROBE_MAX (1 << 24)
-attn_status_t attn_tile_order_probe(int32_t units, int32_t tiles, int32_t reverse, int32_t cluster, int32_t* unit_out,
+attn_status_t attn_tile_order_probe(int32_t units, int32_t tiles, int32_t reverse, int32_t order, int32_t* unit_out,
                                     int32_t* tile_out, size_t n);
 
 #ifdef __cplusplus

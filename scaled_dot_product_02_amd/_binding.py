@@ -458,14 +458,17 @@ def attn_lds_probe(kind, lane_addr, iters, out, stream=None):
         _raise(st)
 
 
-def attn_tile_order_probe(units, tiles, reverse=False, cluster=True):
+ORDERS = {"tile_major": 0, "query": 1, "grouped": 2}
+
+
+def attn_tile_order_probe(units, tiles, reverse=False, order="query"):
     """The kernels' workgroup order (attn_tile_order_probe, evaluated on the host): two lists of
-    units * tiles ints, the unit and the tile of each workgroup index. cluster=True is the order of the
-    query-tile passes (forward, dQ pass), False that of the dK/dV pass."""
+    units * tiles ints, the unit and the tile of each workgroup index. order "query" is that of the
+    forward and the dQ pass, "grouped" of the dense dK/dV passes, "tile_major" of the packed ones."""
     n = int(units) * int(tiles)
     u = (ctypes.c_int32 * max(n, 1))()
     t = (ctypes.c_int32 * max(n, 1))()
-    st = lib().attn_tile_order_probe(int(units), int(tiles), int(bool(reverse)), int(bool(cluster)), u, t, n)
+    st = lib().attn_tile_order_probe(int(units), int(tiles), int(bool(reverse)), ORDERS[order], u, t, n)
     if st != 0:
         _raise(st)
     return list(u)[:n], list(t)[:n]

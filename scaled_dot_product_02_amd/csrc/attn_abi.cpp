@@ -588,15 +588,17 @@ attn_status_t attn_lds_probe(int32_t kind, const int32_t* lane_addr, int32_t ite
   }
 }
 
-attn_status_t attn_tile_order_probe(int32_t units, int32_t tiles, int32_t reverse, int32_t cluster, int32_t* unit_out,
+attn_status_t attn_tile_order_probe(int32_t units, int32_t tiles, int32_t reverse, int32_t order, int32_t* unit_out,
                                     int32_t* tile_out, size_t n) {
+  static_assert(ATTN_ORDER_TILE_MAJOR == sdpa::kOrderTileMajor && ATTN_ORDER_QUERY == sdpa::kOrderQuery &&
+                    ATTN_ORDER_GROUPED == sdpa::kOrderGrouped, "order codes");
   if (units < 1 || tiles < 1 || (int64_t)units * tiles > ATTN_TILE_ORDER_PROBE_MAX)
     return fail(ATTN_E_INVALID, "units %d x tiles %d is not in [1, %d]", units, tiles, ATTN_TILE_ORDER_PROBE_MAX);
-  if ((reverse != 0 && reverse != 1) || (cluster != 0 && cluster != 1))
-    return fail(ATTN_E_INVALID, "reverse and cluster must be 0 or 1");
+  if (reverse != 0 && reverse != 1) return fail(ATTN_E_INVALID, "reverse must be 0 or 1");
+  if (order < ATTN_ORDER_TILE_MAJOR || order > ATTN_ORDER_GROUPED) return fail(ATTN_E_INVALID, "unknown order %d", order);
   if (!unit_out || !tile_out) return fail(ATTN_E_INVALID, "unit_out or tile_out is NULL");
   if (n != (size_t)units * (size_t)tiles) return fail(ATTN_E_INVALID, "n = %zu, units x tiles = %lld", n, (long long)units * tiles);
-  for (int i = 0; i < units * tiles; ++i) sdpa::tile_map_host(i, units, tiles, reverse != 0, cluster != 0, unit_out + i, tile_out + i);
+  for (int i = 0; i < units * tiles; ++i) sdpa::tile_map_host(i, units, tiles, reverse != 0, order, unit_out + i, tile_out + i);
   return ATTN_OK;
 }
 

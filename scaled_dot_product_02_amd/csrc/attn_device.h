@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_internal.h"
+
 namespace sdpa {
 
 typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
@@ -212,24 +214,25 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // one engine; with packed sequences of unequal length one engine then gets several times the
 // average work (measured: the packed Hkv8 dK/dV pass ran at half the dense rate). Each tile row is
 // therefore rotated by 8 units: a unit keeps its XCD and its tiles cycle through the engines.
-// cluster (the query-tile passes: forward, dQ) changes the order when units is a multiple of 8, so that
-// a unit keeps one XCD and its tiles run close together in time there, sharing their K/V through that
-// XCD's L2:
-//  - few tiles per unit (short sequences): unit-major inside each XCD. Workgroup i still runs on XCD
+// The other orders (kOrderQuery: the forward and the dQ pass; kOrderGrouped: the dK/dV passes of dense
+// batches) apply when units is a multiple of 8, so that a unit keeps one XCD and its tiles run close
+// together in time there, sharing their K/V (Q/dO) through that XCD's L2:
+//  - kOrderQuery, few tiles per unit (short sequences): unit-major inside each XCD. Workgroup i still runs on XCD
 //    i % 8, and that XCD's consecutive workgroups take the tiles of one unit; tile-major order would
 //    start a unit's second tile only after every unit's first, long after its K/V left the L2.
 //    Measured on B128 H16 S256 D128: forward -9 %, dQ pass -7 %.
-//  - more than kUnitsInFlight units per XCD: the XCD's units are taken kUnitsInFlight at a time, and
+//  - both, more than kUnitsInFlight units per XCD: the XCD's units are taken kUnitsInFlight at a time, and
 //    each such group runs tile-major (longest tile first, each tile row rotated by one unit across
 //    the shader engines). Plain tile-major order spreads every round over all of the XCD's units, so
 //    their K/V no longer fits the caches once an XCD holds many units; plain unit-major order runs
 //    all of one unit's tiles at once, which measured slower on few long units (dense B2 H16 S8192:
 //    forward +7 %). Measured against tile-major (same-run A/B): B8 H32 S4096 D128 forward -19 %, dQ
 //    pass -17 %; the packed batch of 16 sequences U{256..4096}, H32/8 forward -6 %; B4 H32/8 S8192
-//    dQ pass -4.5 %; groups of 2 or 8 units measured within 2 % of 4. With at most kUnitsInFlight
-//    units per XCD the order is tile-major as before.
-// The dK/dV pass (Q/dO shared by a unit's key tiles) ran 2.6 % slower unit-major on short sequences
-// and keeps tile-major order.
+//    dQ pass -4.5 %; groups of 2 or 8 units measured within 2 % of 4; the dK/dV pass of B8 H32 S4096
+//    -8 %. With at most kUnitsInFlight units per XCD the order is tile-major as before.
+// The dK/dV pass (Q/dO shared by a unit's key tiles) ran 2.6 % slower unit-major on short sequences, and
+// grouped, its packed batches lose the longest-first rounds that end_aligned gives them (the packed
+// batch of 16 sequences: +11 %): packed dK/dV passes keep tile-major order (kOrderTileMajor).
 constexpr int kFewTiles = 4;
 constexpr int kUnitsInFlight = 4;
 // Key-tile passes (dK/dV): round t of tile_order's order takes, for a unit whose sequence has ceil(len /
@@ -243,13 +246,13 @@ __device__ __forceinline__ int end_aligned(int t, int n_tiles, int len, int tile
 }
 // The (unit, tile) of workgroup i (0 <= i < units * tiles; a bijection onto units x tiles). Host and device:
 // the library's attn_tile_order_probe evaluates the same function on the host.
-__host__ __device__ __forceinline__ void tile_map(int i, int units, int tiles, bool reverse, bool cluster, int& unit,
+__host__ __device__ __forceinline__ void tile_map(int i, int units, int tiles, bool reverse, int order, int& unit,
                                                   int& tile) {
-  if (cluster && units % 8 == 0 && tiles <= kFewTiles) {
+  if (order == kOrderQuery && units % 8 == 0 && tiles <= kFewTiles) {
     const int k = i / 8;
     unit = (k / tiles) * 8 + i % 8;
     tile = k % tiles;
-  } else if (cluster && units % 8 == 0 && units / 8 > kUnitsInFlight) {
+  } else if (order != kOrderTileMajor && units % 8 == 0 && units / 8 > kUnitsInFlight) {
     const int k = i / 8;                               // position in XCD i % 8's sequence
     const int c = k / (kUnitsInFlight * tiles);        // group of units
     const int left = units / 8 - kUnitsInFlight * c;   // units of this XCD from group c on
@@ -263,9 +266,8 @@ __host__ __device__ __forceinline__ void tile_map(int i, int units, int tiles, b
   }
   if (reverse) tile = tiles - 1 - tile;
 }
-__device__ __forceinline__ void tile_order(int units, int tiles, bool reverse, int& unit, int& tile,
-                                           bool cluster = false) {
-  tile_map(blockIdx.x, units, tiles, reverse, cluster, unit, tile);
+__device__ __forceinline__ void tile_order(int units, int tiles, bool reverse, int& unit, int& tile, int order) {
+  tile_map(blockIdx.x, units, tiles, reverse, order, unit, tile);
 }
 // Query-side units (forward, dQ pass) are q-heads in (sequence, q-head) order, so consecutive
 // q-heads, including the heads of one GQA group, run on different XCDs. Measured on the packed

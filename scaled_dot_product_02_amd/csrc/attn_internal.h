@@ -5,6 +5,9 @@
 
 namespace sdpa {
 
+// Workgroup orders of tile_map (attn_device.h); the values are those of attn_probe.h's ATTN_ORDER_*.
+constexpr int kOrderTileMajor = 0, kOrderQuery = 1, kOrderGrouped = 2;
+
 // Addressing of one [sequence, head, D] tensor. Element (b, s, h, d) of a dense tensor lives at
 // base + b*batch + s*row + h*head + d; for a packed tensor the sequence start token cu[b] replaces
 // the batch term: base + (cu[b] + s)*row + h*head + d.
@@ -91,7 +94,7 @@ int launch_merge(int dtype, int head_dim, const MergeArgs& a, void* stream);
 // Matrix-core rate probe (attn_probe.hip): blocks x 256 threads, iters rounds of four MFMAs per wave.
 int launch_lds_probe(int kind, const int32_t* lane_addr, int iters, int32_t* out, void* stream);
 // attn_device.h's workgroup order, evaluated on the host (attn_tile_order_probe)
-void tile_map_host(int i, int units, int tiles, bool reverse, bool cluster, int* unit, int* tile);
+void tile_map_host(int i, int units, int tiles, bool reverse, int order, int* unit, int* tile);
 int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsigned long long* ticks,
                       void* stream);
 int fwd_query_tile(int head_dim);

@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(256, MINW) attn_fwd_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int hh = lane >> 5, lrow = lane & 31;
   int u, qt, b, h;
-  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, true);
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, kOrderQuery);
   q_unit(u, s.batch, s.hkv, s.group, b, h);
   const int g = h / s.group;
   const Seq sq = seq_info(s, b);
@@ -475,7 +475,7 @@ __global__ void __launch_bounds__(512, 1) attn_fwd_split_kernel(FwdArgs a) {
   const int pw = w & 3, hf = w >> 2;
   const int hh = lane >> 5, lrow = lane & 31;
   int u, qt, b, h;
-  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, true);
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, kOrderQuery);
   q_unit(u, s.batch, s.hkv, s.group, b, h);
   const int g = h / s.group;
   const Seq sq = seq_info(s, b);
@@ -715,7 +715,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
   int u, kt;
-  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
+  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt, packed ? kOrderTileMajor : kOrderGrouped);
   const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
   kt = end_aligned(kt, a.n_kvtiles, sq.skv, BKV);
@@ -988,7 +988,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
   int u, qt, b, h;
-  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, true);
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, kOrderQuery);
   q_unit(u, s.batch, s.hkv, s.group, b, h);
   const int g = h / s.group;
   const Seq sq = seq_info(s, b);
@@ -1222,7 +1222,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int pr = w & 3, role = w >> 2;  // role 0: K, S, P, dV; role 1: V, dP, dS, dK
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
   int u, kt;
-  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
+  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt, packed ? kOrderTileMajor : kOrderGrouped);
   const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
   kt = end_aligned(kt, a.n_kvtiles, sq.skv, BKV);
@@ -1401,7 +1401,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
   const int pr = w & 3, role = w >> 2;  // role 0: Q, S, P; role 1: dO, dP. Role r accumulates dQ columns [r*DH, r*DH + DH)
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
   int u, qt, b, h;
-  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, true);
+  tile_order(s.batch * s.hq, s.n_qtiles, s.mask != 0, u, qt, kOrderQuery);
   q_unit(u, s.batch, s.hkv, s.group, b, h);
   const int g = h / s.group;
   const Seq sq = seq_info(s, b);
@@ -1591,7 +1591,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_fused_kernel(BwdArgs a) {
   const int pr = w & 3, role = w >> 2;
   const int G = lane >> 4, l16 = lane & 15, rr = (lane >> 2) & 3, cc = lane & 3;
   int u, kt;
-  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt);
+  tile_order(s.batch * s.hkv, a.n_kvtiles, false, u, kt, packed ? kOrderTileMajor : kOrderGrouped);
   const int b = u / s.hkv, g = u % s.hkv;
   const Seq sq = seq_info(s, b);
   kt = end_aligned(kt, a.n_kvtiles, sq.skv, BKV);

@@ -113,9 +113,9 @@ int launch_mfma_probe(int blocks, int iters, float x, float y, float* out, unsig
   return (int)hipGetLastError();
 }
 
-void tile_map_host(int i, int units, int tiles, bool reverse, bool cluster, int* unit, int* tile) {
+void tile_map_host(int i, int units, int tiles, bool reverse, int order, int* unit, int* tile) {
   int u = 0, t = 0;
-  tile_map(i, units, tiles, reverse, cluster, u, t);
+  tile_map(i, units, tiles, reverse, order, u, t);
   *unit = u;
   *tile = t;
 }

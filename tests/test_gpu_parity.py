@@ -75,13 +75,15 @@ def test_packed_sweep(d, dtype, mask, lens):
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
 
 
-# Query-side launches with more than four units per XCD (a unit count that is a multiple of 8, above 32)
-# and more than four query tiles per unit take each XCD's units four at a time; these cases end on a
-# partial group (5, 9 and 6 units per XCD) and are compared whole against the oracle.
+# Launches with more than four units per XCD (a unit count that is a multiple of 8, above 32) take each
+# XCD's units four at a time: the forward and the dQ pass with more than four query tiles per unit, the
+# dK/dV pass of dense batches. These cases end on partial groups (5, 9, 6 units per XCD) on the query
+# side, the dK/dV side or both, and are compared whole against the oracle.
 GROUPED_CASES = [
     dict(batch=5, hq=8, hkv=8, sq=640, skv=640, d=64, dtype="bf16", mask="causal_tl"),
     dict(batch=3, hq=24, hkv=8, sq=600, skv=700, d=128, dtype="fp16", mask="causal_br"),
     dict(hq=8, hkv=4, d=64, dtype="bf16", mask="causal_tl", seqlens=(700, 513, 640, 129, 900, 1)),
+    dict(batch=9, hq=16, hkv=8, sq=300, skv=300, d=64, dtype="fp16", mask="none"),
 ]
 
 

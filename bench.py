@@ -50,9 +50,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "c7b4ddc99427", "bytes": 887811064},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "4d16cc8f8bb4", "bytes": 964519174},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "587643b4bde5", "bytes": 696071034},
+    ("dense_d128", "fwd"): {"fingerprint": "ffc3616327b3", "bytes": 863811757},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "7509116ac4b7", "bytes": 904160977},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "209d84abb105", "bytes": 740881825},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 

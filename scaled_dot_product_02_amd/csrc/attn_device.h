@@ -231,8 +231,9 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 //    dQ pass -4.5 %; groups of 2 or 8 units measured within 2 % of 4; the dK/dV pass of B8 H32 S4096
 //    -8 %. With at most kUnitsInFlight units per XCD the order is tile-major as before.
 // The dK/dV pass (Q/dO shared by a unit's key tiles) ran 2.6 % slower unit-major on short sequences, and
-// grouped, its packed batches lose the longest-first rounds that end_aligned gives them (the packed
-// batch of 16 sequences: +11 %): packed dK/dV passes keep tile-major order (kOrderTileMajor).
+// grouped, the packed batch of 16 sequences ran 11 % slower (also with the units sorted by sequence
+// length first, so not for want of its longest-first rounds): packed dK/dV passes keep tile-major order
+// (kOrderTileMajor).
 constexpr int kFewTiles = 4;
 constexpr int kUnitsInFlight = 4;
 // Key-tile passes (dK/dV): round t of tile_order's order takes, for a unit whose sequence has ceil(len /

@@ -50,25 +50,33 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "ffc3616327b3", "bytes": 863811757},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "7509116ac4b7", "bytes": 904160977},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "209d84abb105", "bytes": 740881825},
+    ("dense_d128", "fwd"): {"fingerprint": "bab9fe12e640", "bytes": 863811757},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "2b18aae84e66", "bytes": 904160977},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "e59198264b6b", "bytes": 740881825},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
 
+def _code_only(text):
+    """The source without its comments and blank lines (a comment edit leaves a fingerprint unchanged)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_fingerprint(kernel):
-    """sha1 prefix of what decides one kernel's code: attn_device.h, attn_internal.h, the shared part of
-    attn_kernels.hip before its first kernel, the kernel's own definition, and the tile-size helpers the
-    launchers instantiate it with."""
+    """sha1 prefix of what decides one kernel's code, comments left out: attn_device.h, attn_internal.h, the
+    shared part of attn_kernels.hip before its first kernel, the kernel's own definition, and the tile-size
+    helpers the launchers instantiate it with."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "scaled_dot_product_02_amd", "csrc")
     src = open(os.path.join(csrc, "attn_kernels.hip")).read()
-    parts = [open(os.path.join(csrc, f)).read() for f in ("attn_device.h", "attn_internal.h")]
-    parts.append(src[:src.index("__global__")])
+    parts = [_code_only(open(os.path.join(csrc, f)).read()) for f in ("attn_device.h", "attn_internal.h")]
+    parts.append(_code_only(src[:src.index("__global__")]))
     m = re.search(r"__global__ void[^\n]*\b" + re.escape(kernel) + r"\(.*?\n}\n", src, re.S)
-    parts.append(m.group(0) if m else "")
+    parts.append(_code_only(m.group(0)) if m else "")
     parts += re.findall(r"template <int D> constexpr int \w+\(\) \{[^\n]*\}", src)
     return hashlib.sha1("\n".join(parts).encode()).hexdigest()[:12]
 

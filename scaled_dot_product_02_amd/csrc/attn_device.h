@@ -226,10 +226,10 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 //    the shader engines). Plain tile-major order spreads every round over all of the XCD's units, so
 //    their K/V no longer fits the caches once an XCD holds many units; plain unit-major order runs
 //    all of one unit's tiles at once, which measured slower on few long units (dense B2 H16 S8192:
-//    forward +7 %). Measured against tile-major (same-run A/B): B8 H32 S4096 D128 forward -19 %, dQ
-//    pass -17 %; the packed batch of 16 sequences U{256..4096}, H32/8 forward -6 %; B4 H32/8 S8192
-//    dQ pass -4.5 %; groups of 2 or 8 units measured within 2 % of 4; the dK/dV pass of B8 H32 S4096
-//    -8 %. With at most kUnitsInFlight units per XCD the order is tile-major as before.
+//    forward +7 %). Measured against tile-major everywhere (same-run A/B, bit-identical results):
+//    B8 H32 S4096 D128 forward -27 %, dQ pass -19 %, dK/dV pass -14 %; the packed batch of 16 sequences
+//    U{256..4096}, H32/8 forward -7 %; B4 H32/8 S8192 dQ pass -4.5 %; groups of 2 or 8 units measured
+//    within 2 % of 4. With at most kUnitsInFlight units per XCD the order is tile-major as before.
 // The dK/dV pass (Q/dO shared by a unit's key tiles) ran 2.6 % slower unit-major on short sequences, and
 // grouped, the packed batch of 16 sequences ran 11 % slower (also with the units sorted by sequence
 // length first, so not for want of its longest-first rounds): packed dK/dV passes keep tile-major order

@@ -584,7 +584,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported (no multi-GPU path "
-              "is built: sharding is described in the design notes, not implemented)", file=sys.stderr)
+              "is built: sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -28,7 +28,7 @@ Sources (the pages, by title and section):
        Stats tensor is [tq, h, 1] for packed thd inputs and [b, h, sq, 1] for
        bshd/sbhd; the attention scale is an fp32 scalar passed by value.
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
   * causal top-left (TL): key j is allowed for query i iff j <= i.
     causal bottom-right (BR): j <= i + (Skv - Sq), per sequence.  [P1 Approach,
     Scope name both; the diagonals are the standard ones, pinned by the TL==BR

@@ -20,7 +20,8 @@
  *
  * Ownership: the caller allocates every buffer (inputs, outputs, workspace). The library allocates
  * nothing, frees nothing, never synchronises, keeps no pointer after a call returns and holds no
- * global mutable state apart from a thread-local error string. Calls on different streams are
+ * global mutable state apart from a thread-local error string and the device array that
+ * attn_bwd_noalloc uses in place of a caller workspace (see there). Calls on different streams are
  * independent as long as their outputs and workspaces are distinct.
  *
  * Errors: every problem that is knowable on the host is reported before any launch, as a status

@@ -84,6 +84,8 @@ GROUPED_CASES = [
     dict(batch=3, hq=24, hkv=8, sq=600, skv=700, d=128, dtype="fp16", mask="causal_br"),
     dict(hq=8, hkv=4, d=64, dtype="bf16", mask="causal_tl", seqlens=(700, 513, 640, 129, 900, 1)),
     dict(batch=9, hq=16, hkv=8, sq=300, skv=300, d=64, dtype="fp16", mask="none"),
+    dict(batch=5, hq=16, hkv=8, sq=200, skv=200, d=512, dtype="fp16", mask="causal_tl"),  # D = 512 pair kernels
+    dict(batch=6, hq=8, hkv=8, sq=700, skv=700, d=256, dtype="bf16", mask="causal_br"),
 ]
 
 

@@ -266,7 +266,7 @@ def atomic_supported(w):
     return max(w.d, w.d_v) <= 128
 
 
-def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False, exp_split=False):
+def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False, exp_split=False, stored_ds=False):
     """Time `steps` steps of workload w. With flush_mall, a 512 MiB buffer is overwritten before every
     timed step (outside the per-kernel events), so no input is still in the 256 MB memory-side cache
     when a step starts; ms_step then includes the fill and only the per-kernel times are meaningful."""
@@ -300,6 +300,10 @@ def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False, exp_
         p.flags = sd.FLAG_BWD_ATOMIC_DQ
         wsb = torch.empty(sd.attn_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
         kw["atomic_dq"] = True
+    if stored_ds:  # stored-dS backward (head dims above 256): preprocess, dK/dV storing dS, dQ = dS K
+        p.flags = sd.FLAG_BWD_STORED_DS
+        wsb = torch.empty(sd.attn_bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        kw["stored_ds"] = True
 
     def step(ev=None):
         def mark(i):
@@ -307,7 +311,7 @@ def run(w, steps, warmup, want_events=True, flush_mall=False, atomic=False, exp_
                 ev[i].record()
         mark(0)
         sd.attn_fwd(q, k, v, out=o, lse=lse, workspace=wsf, exp_split=exp_split,
-                    **{n: a for n, a in kw.items() if n != "atomic_dq"})
+                    **{n: a for n, a in kw.items() if n not in ("atomic_dq", "stored_ds")})
         for i, pas in enumerate(seq):
             mark(1 + i)
             sd.attn_bwd(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, workspace=wsb, passes=(pas,), **kw)

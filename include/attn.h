@@ -146,6 +146,21 @@ typedef struct attn_problem {
  * flag. */
 #define ATTN_FLAG_FWD_EXP_SPLIT 2
 
+/* Stored-dS backward (pull request 3527, section Approach: dQ is the product of dS with K; section Known
+ * limitations: the backward workspace there grows super-linearly, the price this mode pays too). With the
+ * flag the dK/dV pass also stores dS = P * (dP - D), rounded to dtype, for every allowed (query, key) pair
+ * into the workspace, and the dQ pass becomes the product dQ = scale * dS K over each query row's allowed
+ * keys, instead of recomputing S and dP (2 * head_dim FLOP per pair instead of 6 * head_dim). Results are
+ * deterministic; dQ agrees with the default backward to the rounding of its summation order, dK and dV
+ * are bitwise the default ones. Head dims above 256 (head_dim or head_dim_v), the instances whose dQ
+ * recompute costs more than reading dS back; narrower heads are ATTN_E_UNSUPPORTED. The workspace grows
+ * by 2 * heads_q * (query tokens) * ceil(max_seqlen_kv / 64) * 64 bytes (about 2.1 GB for 16 heads at
+ * 8192 x 8192), so attn_bwd_noalloc takes only small problems with it. With the flag the passes run as
+ * attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq, in that order (dq reads the dS that dkdv stored in the
+ * same workspace); attn_bwd runs the three; attn_bwd_dq_preprocess is ATTN_E_UNSUPPORTED. The forward
+ * ignores the flag. */
+#define ATTN_FLAG_BWD_STORED_DS 4
+
 /* Workspace (pull request 3705, section Execution and supported scope: the caller binds the workspace
  * on every call; pull request 3527, section Known limitations: the backward workspace there grows
  * super-linearly, here it is linear in tokens). Its first 256 bytes are a header whose int32 at
@@ -156,8 +171,10 @@ typedef struct attn_problem {
  * keys), so no pre-clearing is needed and a stale word from another call is never trusted. Dense
  * calls neither read nor write it. Dense forward calls need no workspace (0 bytes; ws may be NULL).
  * The backward workspace is linear in the number of query tokens: header + two fp32 [Hq x tokens]
- * arrays (row sums D = rowsum(dO * O), and LSE in log2 units), and with ATTN_FLAG_BWD_ATOMIC_DQ an fp32
- * [tokens x Hq x head_dim] dQ buffer. Sizes are multiples of 256. */
+ * arrays (row sums D = rowsum(dO * O), and LSE in log2 units), with ATTN_FLAG_BWD_ATOMIC_DQ an fp32
+ * [tokens x Hq x head_dim] dQ buffer, and with ATTN_FLAG_BWD_STORED_DS a dtype [Hq x tokens x
+ * ceil(max_seqlen_kv / 64) * 64] dS array (the one workspace that is not linear in tokens). Sizes are
+ * multiples of 256. */
 size_t attn_fwd_workspace_bytes(const attn_problem_t* p);
 size_t attn_bwd_workspace_bytes(const attn_problem_t* p);
 

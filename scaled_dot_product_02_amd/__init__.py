@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     ABI_VERSION,
     FLAG_BWD_ATOMIC_DQ,
     FLAG_FWD_EXP_SPLIT,
+    FLAG_BWD_STORED_DS,
     AttnError,
     AttnProblem,
     attn_bwd,

@@ -17,6 +17,7 @@ LIB_NAME = "libsdpa02.so"
 ABI_VERSION = 4
 FLAG_BWD_ATOMIC_DQ = 1  # ATTN_FLAG_BWD_ATOMIC_DQ
 FLAG_FWD_EXP_SPLIT = 2  # ATTN_FLAG_FWD_EXP_SPLIT
+FLAG_BWD_STORED_DS = 4  # ATTN_FLAG_BWD_STORED_DS
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_ALIGN", 4: "ATTN_E_OVERLAP",
           5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP"}
 MASK_CODES = {"none": 0, "causal_tl": 1, "causal_br": 2}
@@ -301,7 +302,7 @@ def attn_fwd(q, k, v, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlen
 
 def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None,
              max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
-             passes=("all",), window_left=-1, atomic_dq=False):
+             passes=("all",), window_left=-1, atomic_dq=False, stored_ds=False):
     """Backward through the C-ABI from the forward's O and LSE. Returns (dQ, dK, dV).
 
     dO must have O's strides; dQ/dK/dV are allocated with Q/K/V's shapes (contiguous) unless given.
@@ -309,7 +310,10 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
     "dkdv", "dq", "dq_preprocess" (attn_bwd_preprocess / attn_bwd_dkdv / attn_bwd_dq /
     attn_bwd_dq_preprocess, which share the workspace; "dq_preprocess" then "dkdv" is what
     attn_bwd runs for head dims up to 256). ``atomic_dq`` sets ATTN_FLAG_BWD_ATOMIC_DQ (the single-pass
-    backward, head dims up to 128): then "preprocess", "dkdv", "dq" is what attn_bwd runs.
+    backward, head dims up to 128): then "preprocess", "dkdv", "dq" is what attn_bwd runs. ``stored_ds`` sets
+    ATTN_FLAG_BWD_STORED_DS (dS stored by the dK/dV pass, dQ as its product with K; head dims above 256;
+    the workspace then holds Hq x tokens x max_seqlen_kv (rounded up to 64) dS values): "preprocess",
+    "dkdv", "dq" again.
     """
     import torch
     _check_tensors(q, k, v, cu_seqlens_q is not None, cu_seqlens_q, cu_seqlens_kv, o=o, do=do, lse=lse, dq=dq,
@@ -325,7 +329,7 @@ def attn_bwd(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=Non
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("dQ/dK/dV must have the strides of Q/K/V")
     p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                     window_left, FLAG_BWD_ATOMIC_DQ if atomic_dq else 0)
+                     window_left, (FLAG_BWD_ATOMIC_DQ if atomic_dq else 0) | (FLAG_BWD_STORED_DS if stored_ds else 0))
     L = lib()
     need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
     ws = _workspace(need, q.device, workspace)

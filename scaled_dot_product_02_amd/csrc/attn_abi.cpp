@@ -79,6 +79,8 @@ bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 // Head dims (pull request 3527, section Scope: any multiple of 8 up to 512, padded to a compiled
 // width; an asymmetric Q/K vs V/O pair). head_dim_v = 0 means the same as head_dim.
 int head_dim_v(const attn_problem_t* p) { return p->head_dim_v ? p->head_dim_v : p->head_dim; }
+// keys per stored dS row of the stored-dS backward: the longest key range rounded up to 64
+int64_t ds_row(const attn_problem_t* p) { return ((int64_t)p->max_seqlen_kv + 63) / 64 * 64; }
 
 attn_status_t check_head_dims(const attn_problem_t* p) {
   if (p->head_dim <= 0) return fail(ATTN_E_INVALID, "head_dim %d <= 0", p->head_dim);
@@ -108,7 +110,7 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   if (!(p->scale > 0.f)) return fail(ATTN_E_UNSUPPORTED, "scale %g is not positive", (double)p->scale);
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0) return fail(ATTN_E_INVALID, "negative max_seqlen");
   if (p->window_left < -1) return fail(ATTN_E_INVALID, "window_left %d < -1", p->window_left);
-  if (p->flags & ~(ATTN_FLAG_BWD_ATOMIC_DQ | ATTN_FLAG_FWD_EXP_SPLIT))
+  if (p->flags & ~(ATTN_FLAG_BWD_ATOMIC_DQ | ATTN_FLAG_FWD_EXP_SPLIT | ATTN_FLAG_BWD_STORED_DS))
     return fail(ATTN_E_INVALID, "unknown flags 0x%x", (unsigned)p->flags);
   if (p->window_left >= 0 && p->mask == ATTN_MASK_NONE)
     return fail(ATTN_E_UNSUPPORTED, "window_left %d needs a causal mask (the window is measured from its diagonal)",
@@ -151,6 +153,10 @@ attn_status_t check_problem(const attn_problem_t* p, Info* info) {
   info->packed = packed;
   info->nq = packed ? p->total_q : (int64_t)p->batch * p->max_seqlen_q;
   info->nkv = packed ? p->total_kv : (int64_t)p->batch * p->max_seqlen_kv;
+  // the stored-dS array (2 bytes per query token, head and stored key) must stay below 2^62 bytes
+  if ((p->flags & ATTN_FLAG_BWD_STORED_DS) && info->nq > 0 &&
+      ds_row(p) > (int64_t(1) << 61) / (info->nq * p->heads_q))
+    return fail(ATTN_E_UNSUPPORTED, "the stored-dS workspace (ATTN_FLAG_BWD_STORED_DS) exceeds 2^62 bytes");
   return ATTN_OK;
 }
 
@@ -268,6 +274,7 @@ size_t attn_bwd_workspace_bytes(const attn_problem_t* p) {
   if (check_problem(p, &in) != ATTN_OK) return 0;
   size_t n = kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float));
   if (p->flags & ATTN_FLAG_BWD_ATOMIC_DQ) n += round256((size_t)in.nq * p->heads_q * p->head_dim * sizeof(float));
+  if (p->flags & ATTN_FLAG_BWD_STORED_DS) n += round256((size_t)in.nq * p->heads_q * ds_row(p) * 2);
   return n;
 }
 
@@ -382,6 +389,13 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     if (atomic && passes == sdpa::kPassDqPre)
       return fail(ATTN_E_UNSUPPORTED, "attn_bwd_dq_preprocess has no single-pass form (ATTN_FLAG_BWD_ATOMIC_DQ): "
                   "call attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq");
+    const bool stored_ds = (p->flags & ATTN_FLAG_BWD_STORED_DS) != 0;
+    if (stored_ds && sdpa::instance_head_dim(dqk, dvw) <= 256)
+      return fail(ATTN_E_UNSUPPORTED, "the stored-dS backward (ATTN_FLAG_BWD_STORED_DS) is built for head dims above "
+                  "256; head_dim %d, head_dim_v %d", dqk, dvw);
+    if (stored_ds && passes == sdpa::kPassDqPre)
+      return fail(ATTN_E_UNSUPPORTED, "attn_bwd_dq_preprocess has no stored-dS form (ATTN_FLAG_BWD_STORED_DS): "
+                  "call attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq");
     sdpa::BwdArgs a{};
     const int inst = sdpa::instance_head_dim(dqk, dvw);
     a.s = make_shape(p, in, ws, sdpa::bwd_query_tile(inst));
@@ -406,6 +420,11 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     a.atomic_dq = atomic ? 1 : 0;
     a.dq_acc = atomic ? (float*)((char*)ws + kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float)))
                       : nullptr;
+    a.ds = stored_ds
+               ? (unsigned short*)((char*)ws + kHeader + 2 * round256((size_t)in.nq * p->heads_q * sizeof(float)))
+               : nullptr;
+    a.ds_ld = ds_row(p);
+    a.n_dsqtiles = (p->max_seqlen_q + 63) / 64;
     a.aq = addr(p->q_stride, in.packed);
     a.ak = addr(p->k_stride, in.packed);
     a.av = addr(p->v_stride, in.packed);

@@ -30,6 +30,8 @@ typedef __bf16 v4bf __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef _Float16 v4h __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef float v16f __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
+typedef unsigned v4u __attribute__((__vector_size__(4 * sizeof(unsigned))));
+typedef unsigned v2u __attribute__((__vector_size__(2 * sizeof(unsigned))));
 
 typedef __attribute__((address_space(3))) void lds_void;
 

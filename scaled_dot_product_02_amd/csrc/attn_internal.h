@@ -62,6 +62,12 @@ struct BwdArgs {
   int32_t n_kvtiles;  // ceil(skv / key tile) of the dK/dV kernel
   int32_t atomic_dq;  // single-pass backward: dQ accumulated in dq_acc with fp32 atomics
   float* dq_acc;      // workspace (atomic_dq only): fp32 [nrows][hq][dqk]
+  // stored-dS backward (D = 512 instances): the dK/dV pass stores dS (in dtype) into ds, and the dQ pass
+  // is the product dQ = scale * dS K. ds: workspace [hq][nrows][ds_ld]; ds_ld = max key length rounded
+  // up to 64; n_dsqtiles = ceil(sq / 64), the query tiles of that product. nullptr: recompute dQ.
+  unsigned short* ds;
+  int64_t ds_ld;
+  int32_t n_dsqtiles;
 };
 
 // Merge of per-chunk results (attn_merge): nrows = query rows * hq independent (row, head) pairs.

@@ -1275,8 +1275,29 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   const int rrow = l16 * D, rkey = (sw_key<D>(l16) ^ G) << 3;
   const int trow = (4 * G + rr) * D + 4 * (cc & 1), tkey = (sw_key<D>(4 * G + rr) ^ (cc >> 1)) << 3;
   float* pbuf = xch + pr * 2 * 64 * 4;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;  // the sequence's first query token
 
-  int qt_c = qt0;  // query tile of the iteration
+  int qt_c = qt0, hq_c = g * s.group;  // query tile and q-head of the iteration
+
+  // stored-dS backward: the dS of an iteration (role 1) is kept in ds_w and written after the next
+  // barrier, so the copy wait before that barrier does not also wait for these stores to complete. Key
+  // 16a + 8c + 4h + j of a 32-key block goes to position 16c + 8h + 4a + j; rows past the sequence end are
+  // not stored.
+  v2u ds_w[2];
+  int ds_qs0 = 0, ds_h = 0;
+  bool ds_pending = false;
+  auto store_ds = [&]() {
+    if (!ds_pending) return;
+    const int j = l16 & 3;
+    const int kl = (kw0 & 31) + l16 - j;  // first key of the lane's quad within its 32-key block
+    const int run = (kw0 - (kw0 & 31)) + (((kl >> 3) & 1) << 4) + (((kl >> 2) & 1) << 3) + ((kl >> 4) << 2);
+    T* dsp = reinterpret_cast<T*>(a.ds) + ((int64_t)ds_h * a.nrows + rowbase + ds_qs0 + 4 * G + j) * a.ds_ld + run;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      if (ds_qs0 + 16 * qb + 4 * G + j < sq.sq)
+        __builtin_nontemporal_store(ds_w[qb], reinterpret_cast<v2u*>(dsp + (int64_t)16 * qb * a.ds_ld));
+    ds_pending = false;
+  };
   if constexpr (PAD) {
     zero_lds<2 * STAGE>(smem);
     __syncthreads();
@@ -1286,6 +1307,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_it) issue((it + 1) & 1);
+    store_ds();
     // per-stage byte bases of this wave's row reads (Q for role 0, dO for role 1) and transpose reads
     // (dO for role 0, Q for role 1): one XOR with a constant per read, the rest in immediate offsets
     const int sbb = 2 * (it & 1) * STAGE;
@@ -1295,8 +1317,13 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     const us* dos = qs + QTILE;
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
     const float* rss = l2s + 64;
-    const int qs0 = qt_c * BQ;
-    qt_c = qt_c + 1 == qt_end ? qt0 : qt_c + 1;
+    const int qs0 = qt_c * BQ, h_c = hq_c;
+    if (qt_c + 1 == qt_end) {
+      qt_c = qt0;
+      ++hq_c;
+    } else {
+      ++qt_c;
+    }
     const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0) &&
                         (s.wl < 0 || qs0 + delta - s.wl <= kw0 + KW - 1);
     const bool need_mask = (qs0 + BQ > sq.sq) || (kw0 + KW > sq.skv) || (s.mask != 0 && qs0 + delta < kw0 + KW - 1) ||
@@ -1358,6 +1385,31 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
       }
     }
     const auto pa = pack8<T>(sv[0][0], sv[0][1], sv[0][2], sv[0][3], sv[1][0], sv[1][1], sv[1][2], sv[1][3]);
+    if (role == 1 && a.ds != nullptr) {
+      // stored-dS backward: dS rounded to T (the values of the dK product). The lane holds rows
+      // qs0 + 16qb + 4G + i (i = 0..3) of key kw0 + l16; a 4 x 4 transpose inside each lane quad (keys
+      // kw0 + 4m + j, j = l16 & 3) leaves lane j with row qs0 + 16qb + 4G + j of those four keys, one
+      // 8-byte run in the order attn_bwd_dq_ds_kernel reads. Stored after the next barrier (store_ds).
+      const auto pw = __builtin_bit_cast(v4u, pa);  // word 2qb + (i >> 1), half i & 1
+      const int j = l16 & 3;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const unsigned w0 = pw[2 * qb], w1 = pw[2 * qb + 1];
+        // lanes j, j ^ 1 swap 16-bit halves: lane j then holds rows 2t + (j & 1) (word t) of keys j & ~1, +1
+        const unsigned n0 = (unsigned)__builtin_amdgcn_update_dpp(0, (int)w0, 0xB1, 0xF, 0xF, false);
+        const unsigned n1 = (unsigned)__builtin_amdgcn_update_dpp(0, (int)w1, 0xB1, 0xF, 0xF, false);
+        const bool odd = j & 1;
+        const unsigned ra = odd ? (n0 >> 16) | (w0 & 0xFFFF0000u) : (w0 & 0xFFFFu) | (n0 << 16);
+        const unsigned rb = odd ? (n1 >> 16) | (w1 & 0xFFFF0000u) : (w1 & 0xFFFFu) | (n1 << 16);
+        // lanes j, j ^ 2 swap words: lane j then holds row j of keys 0..3
+        const bool low = j < 2;
+        const unsigned r = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(low ? rb : ra), 0x4E, 0xF, 0xF, false);
+        ds_w[qb] = low ? v2u{ra, r} : v2u{r, rb};
+      }
+      ds_qs0 = qs0;
+      ds_h = h_c;
+      ds_pending = true;
+    }
     // dV += P^T dO ; dK += dS^T Q
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -1367,6 +1419,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     }
   }
 
+  store_ds();
   T* outp = role == 0 ? (T*)a.dv + seq_off(a.av, packed, b, sq.tk0) + (int64_t)g * a.av.head
                       : (T*)a.dk + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
   const int64_t orow = role == 0 ? a.av.row : a.ak.row;
@@ -1531,6 +1584,148 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
         if (!PAD || role * DH + 16 * dt + l16 < s.dqk)
           dqp[(int64_t)q * a.aq.row + 16 * dt + l16] = Elem<T>::cvt(dq[dt][i] * s.scale);
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ of the stored-dS backward (opt-in, ATTN_FLAG_BWD_STORED_DS, D = 512 instances): the dK/dV pass has
+// stored dS (rounded to T) for every allowed pair, so dQ = scale * dS K is a plain product over each
+// query row's allowed keys, 2*D FLOP per pair instead of the 6*D the recomputing dQ pass executes (its
+// S and dP products are 4*D of them, which at D = 512 take longer than reading the stored dS back).
+// Workgroup = 4 waves = 64 query rows of one (sequence, q-head), two workgroups per CU: wave w takes
+// rows 32*(w%2) .. +31 and dQ columns 256*(w/2) .. +255, as dQ^T += K^T dS^T with 32x32x16 MFMAs (A = K^T
+// by transpose reads of the LDS tile, the same reads as the forward's V^T at D = 256; B = this lane's row
+// of dS, 8 keys per lane, 16 bytes straight from the workspace). Key tiles of 32 keys x 512 columns (two
+// 32 x 256 halves, 64 KB for the two-stage ring) stream through LDS; the dS operands of the next tile are
+// loaded beside its copy. dS is stored in a [q-head][query token][ds_ld] array; inside each 32-key block
+// key 16a + 8c + 4h + j sits at position 16c + 8h + 4a + j, so that the lane (row, half h) of k-step c
+// reads one 16-byte run in the order the K^T operand delivers the keys. The dK/dV pass writes every
+// allowed pair; a tile that holds a pair outside the mask (or past the key range) replaces those dS
+// values by zeros, whatever the workspace holds there.
+template <typename T, bool PAD>
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
+  constexpr int DH = 256, BM = 64, BN = 32;
+  constexpr int TILE = BN * DH;             // 16-bit elements of one key half-tile
+  constexpr int NDMA = TILE * 2 / 1024 / 4;  // 16-byte copies per wave per half
+  static_assert(NDMA >= 1, "half tile must split over 4 waves");
+  __shared__ __attribute__((aligned(1024))) us smem[2 * 2 * TILE];
+  const AttnShape& s = a.s;
+  const bool packed = s.cu_q != nullptr;
+  if (packed && *s.err) {
+    fill_nan_rows<T>(a.dq, a.aq, s.total_q, s.hq, s.dqk);
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int hf = w >> 1, wr = w & 1;  // column half and row block of this wave
+  const int hh = lane >> 5, lrow = lane & 31;
+  int u, qt, b, h;
+  tile_order(s.batch * s.hq, a.n_dsqtiles, s.mask != 0, u, qt, kOrderQuery);
+  q_unit(u, s.batch, s.hkv, s.group, b, h);
+  const int g = h / s.group;
+  const Seq sq = seq_info(s, b);
+  const int q0 = qt * BM;
+  if (q0 >= sq.sq) return;
+  const int delta = s.mask == 2 ? sq.skv - sq.sq : 0;
+  const int kv_end = s.mask != 0 ? min(sq.skv, q0 + BM + delta) : sq.skv;
+  const int n_tiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+  // first key tile inside some row's sliding window (0 without a window)
+  const int j0 = s.wl >= 0 ? max(0, q0 + delta - s.wl) / BN : 0;
+  const int qw0 = q0 + 32 * wr, qi = qw0 + lrow;
+  // a wave whose column half lies wholly past D_qk has nothing to compute (it still copies and waits)
+  const bool cols = hf * DH < s.dqk;
+
+  const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
+  const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
+  // this lane's dS row (rows past the sequence end read the last row and are never stored), from the
+  // k-step's half 8*hh
+  const us* dsr = a.ds + ((int64_t)h * a.nrows + rowbase + min(qi, sq.sq - 1)) * a.ds_ld + 8 * hh;
+  auto load_ds = [&](int tile, v8s* d) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) d[c] = *reinterpret_cast<const v8s*>(dsr + tile * BN + 16 * c);
+  };
+
+  const TileDma<DH, BN, NDMA, true, PAD> dma(w, lane, a.ak.row, a.ak.row, min(s.dqk, DH), max(0, s.dqk - DH));
+  auto issue = [&](int tile, int stage) {
+    us* xs = smem + stage * 2 * TILE;
+    const us* kt = kg + (int64_t)tile * BN * a.ak.row;
+    dma.copy(kt, kt + DH, sq.skv - 1 - tile * BN, xs, xs + TILE);
+  };
+
+  // K^T operand: the forward's V^T transpose reads at D = 256 (k-chunk c: keys 8c + 4hh + 0..3 and the
+  // same + 16), from this wave's column half
+  const int G = lane >> 4, rr = (lane >> 2) & 3, c4 = lane & 3;
+  const int vrow = (4 * hh + rr) * DH + 4 * (c4 & 1);
+  int vb[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    vb[c] = opaque(2 * (vrow + 8 * c * DH + ((sw_key<DH>(8 * c + 4 * hh + rr) ^ (2 * (G & 1) + (c4 >> 1))) << 3))) +
+            hf * 2 * TILE;
+
+  v16f acc[DH / 32];
+#pragma unroll
+  for (int dt = 0; dt < DH / 32; ++dt) acc[dt] = v16f{};
+  if constexpr (PAD) {
+    zero_lds<2 * 2 * TILE>(smem);
+    __syncthreads();
+  }
+  v8s dcur[2], dnext[2];
+  if (j0 < n_tiles) {
+    load_ds(j0, dcur);
+    issue(j0, j0 & 1);
+  }
+  for (int j = j0; j < n_tiles; ++j) {
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      load_ds(j + 1, dnext);
+      issue(j + 1, (j + 1) & 1);
+    }
+    const int kv0 = j * BN;
+    const bool skip = !cols || (s.mask != 0 && kv0 > qw0 + 31 + delta) ||  // tile fully masked for this wave
+                      (s.wl >= 0 && kv0 + BN - 1 < qw0 + delta - s.wl);      // tile before this wave's windows
+    if (!skip) {
+      const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta) ||
+                             (s.wl >= 0 && kv0 < qw0 + 31 + delta - s.wl);
+      v8s d[2] = {dcur[0], dcur[1]};
+      if (need_mask) {  // one branch per tile: element e of k-step c is key kv0 + 16(e/4) + 8c + 4hh + e%4
+        const int lim = min(sq.skv - 1, s.mask == 0 ? sq.skv : qi + delta) - kv0 - 4 * hh;
+        const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);
+        const bool row_ok = qi < sq.sq;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int off = 16 * (e >> 2) + 8 * c + (e & 3);
+            d[c][e] = row_ok && off <= lim && off >= lo ? d[c][e] : (short)0;
+          }
+      }
+      const int sb = (j & 1) * 4 * TILE;  // stage, bytes
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) {
+          const int o1 = (vb[c] ^ (64 * dt)) + sb;
+          const v4s lo = lds_read_tr_at(smem, o1);
+          const v4s hi = lds_read_tr_at(smem, o1 + 32 * DH);
+          acc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), Elem<T>::cast(d[c]), acc[dt]);
+        }
+    }
+    dcur[0] = dnext[0];
+    dcur[1] = dnext[1];
+  }
+
+  if (cols && qi < sq.sq) {
+    T* dqp = (T*)a.dq + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h * a.aq.head + (int64_t)qi * a.aq.row + hf * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        typename Elem<T>::op4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Elem<T>::cvt(acc[dt][4 * q4 + e] * s.scale);
+        if (!PAD || hf * DH + 32 * dt + 8 * q4 + 4 * hh < s.dqk)
+          *reinterpret_cast<typename Elem<T>::op4*>(dqp + 32 * dt + 8 * q4 + 4 * hh) = v;
+      }
   }
 }
 
@@ -2088,6 +2283,9 @@ static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
         hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T, PAD, true>), grid, dim3(256), 0, st, a);
       else
         hipLaunchKernelGGL((attn_bwd_dq_kernel<D, dq_qb<D>(), bwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
+    } else if (a.ds != nullptr) {
+      if (a.n_dsqtiles == 0) return;
+      hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<T, PAD>), dim3(a.s.batch * a.s.hq * a.n_dsqtiles), dim3(256), 0, st, a);
     } else {
       hipLaunchKernelGGL((attn_bwd_dq_pair_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
     }

@@ -64,7 +64,7 @@ def _nan_like(shape, dtype, dev):
     return torch.full(shape, float("nan"), dtype=dtype, device=dev)
 
 
-def gpu_run(w, x, backward=True, stream=None, atomic_dq=False, exp_split=False):
+def gpu_run(w, x, backward=True, stream=None, atomic_dq=False, exp_split=False, stored_ds=False):
     """Forward (and backward) of workload w on cuda:0 through the C-ABI; returns CPU tensors.
 
     Every output buffer starts as NaN, so an element that no kernel writes (or that a kernel writes
@@ -83,7 +83,8 @@ def gpu_run(w, x, backward=True, stream=None, atomic_dq=False, exp_split=False):
     if backward:
         do = x["do"].to(dev)
         grads = {n: _nan_like(t.shape, t.dtype, dev) for n, t in (("dq", q), ("dk", k), ("dv", v))}
-        dq, dk, dv = sd.attn_bwd(q, k, v, o, do, lse, stream=stream, atomic_dq=atomic_dq, **grads, **kw)
+        dq, dk, dv = sd.attn_bwd(q, k, v, o, do, lse, stream=stream, atomic_dq=atomic_dq, stored_ds=stored_ds,
+                                 **grads, **kw)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in out.items()}
@@ -223,8 +224,8 @@ def all_units(w, x):
     return [(b, g) for b in range(nseq) for g in range(w.hkv)]
 
 
-def run_and_check(w, units=None, backward=True, atomic_dq=False, exp_split=False):
+def run_and_check(w, units=None, backward=True, atomic_dq=False, exp_split=False, stored_ds=False):
     x = make_inputs(w)
-    got = gpu_run(w, x, backward=backward, atomic_dq=atomic_dq, exp_split=exp_split)
+    got = gpu_run(w, x, backward=backward, atomic_dq=atomic_dq, exp_split=exp_split, stored_ds=stored_ds)
     assert_all_written(w.name, got)
     return check_units(w, x, got, units if units is not None else all_units(w, x))

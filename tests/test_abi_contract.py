@@ -98,7 +98,7 @@ def test_null_problem(L):
     ("abi_version", 2, UNSUPPORTED, "abi_version"),
     ("abi_version", 3, UNSUPPORTED, "abi_version"),
     ("abi_version", 5, UNSUPPORTED, "abi_version"),
-    ("flags", 4, INVALID, "unknown flags"),
+    ("flags", 8, INVALID, "unknown flags"),
     ("window_left", -2, INVALID, "window_left"),
     ("head_dim_v", -8, INVALID, "head_dim_v"),
     ("head_dim_v", 100, UNSUPPORTED, "head_dim_v 100"),
@@ -439,7 +439,7 @@ def test_single_pass_backward_flag(L):
     and q-head to the backward workspace; head dims past 128 and the fused dQ + preprocess pass are
     declined with a reason, before any launch."""
     p = dense_problem()
-    p.flags = 4
+    p.flags = 8
     expect(L, bwd(L, p), INVALID, "unknown flags")
     p = dense_problem(b=2, sq=256, hq=4, d=128)
     base = L.attn_bwd_workspace_bytes(ctypes.byref(p))
@@ -467,5 +467,39 @@ def test_exp_split_flag(L):
     p.flags = B.FLAG_FWD_EXP_SPLIT
     assert L.attn_fwd_workspace_bytes(ctypes.byref(p)) == base_f
     assert L.attn_bwd_workspace_bytes(ctypes.byref(p)) == base_b
-    p.flags = B.FLAG_FWD_EXP_SPLIT | 4
+    p.flags = B.FLAG_FWD_EXP_SPLIT | 8
     expect(L, fwd(L, p), INVALID, "unknown flags")
+
+
+def test_stored_ds_flag(L):
+    """ATTN_FLAG_BWD_STORED_DS: the flag adds a dtype [Hq x query tokens x max_seqlen_kv rounded up to 64]
+    dS array to the backward workspace (dense and packed); head dims up to 256 and the fused dQ +
+    preprocess pass are declined with a reason before any launch, and a workspace one 256-byte block short
+    is refused."""
+    p = dense_problem(b=2, sq=256, skv=300, hq=4, hkv=2, d=512)
+    base = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    p.flags = B.FLAG_BWD_STORED_DS
+    ds = 2 * 4 * (2 * 256) * 320  # bf16 x heads x tokens x (300 keys rounded up to 64)
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(p)) == base + (ds + 255) // 256 * 256
+    expect(L, L.attn_bwd_dq_preprocess(ctypes.byref(p), Q, K, V, O, DO, LSE, DQ, DK, DV, WS, 1 << 30, None),
+           UNSUPPORTED, "attn_bwd_dq_preprocess")
+    need = L.attn_bwd_workspace_bytes(ctypes.byref(p))
+    expect(L, bwd(L, p, ws_bytes=need - 256), WORKSPACE, "workspace")
+    for d, dv in ((256, 0), (128, 256), (64, 0)):
+        narrow = dense_problem(d=d)
+        narrow.head_dim_v = dv
+        narrow.flags = B.FLAG_BWD_STORED_DS
+        expect(L, bwd(L, narrow), UNSUPPORTED, "head dims above 256")
+    for d, dv in ((64, 512), (512, 96), (264, 0)):  # any head above 256 on either side takes the mode
+        wide = dense_problem(d=d)
+        wide.head_dim_v = dv
+        wide.flags = B.FLAG_BWD_STORED_DS
+        assert L.attn_bwd_workspace_bytes(ctypes.byref(wide)) > 0
+    both = dense_problem(d=512)
+    both.flags = B.FLAG_BWD_STORED_DS | B.FLAG_BWD_ATOMIC_DQ
+    expect(L, bwd(L, both), UNSUPPORTED, "head dims up to 128")
+    # the forward ignores the flag: no workspace change
+    p0 = dense_problem(b=2, sq=256, skv=300, hq=4, hkv=2, d=512)
+    f0 = L.attn_fwd_workspace_bytes(ctypes.byref(p0))
+    p0.flags = B.FLAG_BWD_STORED_DS
+    assert L.attn_fwd_workspace_bytes(ctypes.byref(p0)) == f0

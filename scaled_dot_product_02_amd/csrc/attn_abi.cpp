@@ -393,6 +393,8 @@ attn_status_t bwd_passes(int passes, const attn_problem_t* p, const void* q, con
     if (stored_ds && sdpa::instance_head_dim(dqk, dvw) <= 256)
       return fail(ATTN_E_UNSUPPORTED, "the stored-dS backward (ATTN_FLAG_BWD_STORED_DS) is built for head dims above "
                   "256; head_dim %d, head_dim_v %d", dqk, dvw);
+    if (stored_ds && ds_row(p) >= (int64_t(1) << 24))
+      return fail(ATTN_E_UNSUPPORTED, "the stored-dS backward (ATTN_FLAG_BWD_STORED_DS) takes key lengths below 2^24");
     if (stored_ds && passes == sdpa::kPassDqPre)
       return fail(ATTN_E_UNSUPPORTED, "attn_bwd_dq_preprocess has no stored-dS form (ATTN_FLAG_BWD_STORED_DS): "
                   "call attn_bwd_preprocess, attn_bwd_dkdv, attn_bwd_dq");

@@ -130,6 +130,9 @@ __device__ __forceinline__ void dma4(const void* base, unsigned off, void* lds_w
 // asm, so that the compiler's wait-count tracking sees it (loads issued before it need no further
 // wait after it).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// The same but leaving this wave's most recent vector-memory load in flight (vmcnt = 1; loads complete
+// in issue order).
+__device__ __forceinline__ void wait_vmem_but1() { __builtin_amdgcn_s_waitcnt(0x0F71); }
 
 // LDS tile rows are stored with their 16-byte chunks permuted: physical chunk = logical chunk ^
 // sw_key(row), the key a function of the row's low 4 bits (the readers see rows 16m + r).

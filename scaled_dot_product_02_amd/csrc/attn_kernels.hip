@@ -1199,7 +1199,7 @@ __global__ void __launch_bounds__(256, MINW) attn_bwd_dq_kernel(BwdArgs a) {
 // computes dP, they swap (fp32), both form the same dS, and each accumulates half of dQ's columns.
 // Every wave executes every barrier; a pair whose keys / rows see nothing in a tile skips its MFMAs.
 // ------------------------------------------------------------------------------------------
-template <int D, typename T, bool PAD>
+template <int D, typename T, bool PAD, bool STORE_DS = false>
 __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   constexpr int NW = 8, KW = 16, BKV = 4 * KW, BQ = 32, CH = D / 8;
   constexpr int QTILE = BQ * D;
@@ -1211,6 +1211,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   static_assert((STAGE & (D - 1)) == 0 && 2 * 64 * 2 <= D, "stage padding");
   __shared__ __attribute__((aligned(1024))) us smem[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float xch[4 * 2 * 64 * 4];  // P per pair: [qb][lane][4]
+  __shared__ __attribute__((aligned(16))) us dsst[STORE_DS ? 4 * 32 * 16 : 8];  // STORE_DS: dS per pair, [row][key]
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
@@ -1279,23 +1280,25 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
 
   int qt_c = qt0, hq_c = g * s.group;  // query tile and q-head of the iteration
 
-  // stored-dS backward: the dS of an iteration (role 1) is kept in ds_w and written after the next
-  // barrier, so the copy wait before that barrier does not also wait for these stores to complete. Key
-  // 16a + 8c + 4h + j of a 32-key block goes to position 16c + 8h + 4a + j; rows past the sequence end are
+  // stored-dS backward (STORE_DS, an instance of its own: the default one keeps its registers): the
+  // role-1 wave of a pair puts the dS of an iteration (rounded to T: the values of its dK product) into
+  // its [32 row][16 key] LDS buffer and, after the next barrier, reads it back a row run per lane and
+  // writes it out, so that the copy wait before that barrier does not also wait for these stores and
+  // no register stays live across the S/dP products. Key 16a + 8c + 4h + j of a 32-key block goes to
+  // position 16c + 8h + 4a + j (the order attn_bwd_dq_ds_kernel reads); rows past the sequence end are
   // not stored.
-  v2u ds_w[2];
   int ds_qs0 = 0, ds_h = 0;
   bool ds_pending = false;
   auto store_ds = [&]() {
-    if (!ds_pending) return;
-    const int j = l16 & 3;
-    const int kl = (kw0 & 31) + l16 - j;  // first key of the lane's quad within its 32-key block
-    const int run = (kw0 - (kw0 & 31)) + (((kl >> 3) & 1) << 4) + (((kl >> 2) & 1) << 3) + ((kl >> 4) << 2);
-    T* dsp = reinterpret_cast<T*>(a.ds) + ((int64_t)ds_h * a.nrows + rowbase + ds_qs0 + 4 * G + j) * a.ds_ld + run;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-      if (ds_qs0 + 16 * qb + 4 * G + j < sq.sq)
-        __builtin_nontemporal_store(ds_w[qb], reinterpret_cast<v2u*>(dsp + (int64_t)16 * qb * a.ds_ld));
+    if (!STORE_DS || !ds_pending) return;
+    const int r = lane >> 1, c = lane & 1;  // row r, keys 8c .. 8c + 7 of the pair (runs h = 0, 1)
+    const v8s x = *reinterpret_cast<const v8s*>(dsst + pr * 512 + r * 16 + 8 * c);
+    if (ds_qs0 + r < sq.sq) {
+      T* dsp = reinterpret_cast<T*>(a.ds) + ((int64_t)ds_h * a.nrows + rowbase + ds_qs0 + r) * a.ds_ld +
+               (kw0 - (kw0 & 31)) + 16 * c + 4 * ((kw0 >> 4) & 1);
+      __builtin_nontemporal_store(v4s{x[0], x[1], x[2], x[3]}, reinterpret_cast<v4s*>(dsp));
+      __builtin_nontemporal_store(v4s{x[4], x[5], x[6], x[7]}, reinterpret_cast<v4s*>(dsp + 8));
+    }
     ds_pending = false;
   };
   if constexpr (PAD) {
@@ -1385,37 +1388,41 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
       }
     }
     const auto pa = pack8<T>(sv[0][0], sv[0][1], sv[0][2], sv[0][3], sv[1][0], sv[1][1], sv[1][2], sv[1][3]);
-    if (role == 1 && a.ds != nullptr) {
-      // stored-dS backward: dS rounded to T (the values of the dK product). The lane holds rows
-      // qs0 + 16qb + 4G + i (i = 0..3) of key kw0 + l16; a 4 x 4 transpose inside each lane quad (keys
-      // kw0 + 4m + j, j = l16 & 3) leaves lane j with row qs0 + 16qb + 4G + j of those four keys, one
-      // 8-byte run in the order attn_bwd_dq_ds_kernel reads. Stored after the next barrier (store_ds).
-      const auto pw = __builtin_bit_cast(v4u, pa);  // word 2qb + (i >> 1), half i & 1
-      const int j = l16 & 3;
+    if (STORE_DS && role == 1) {  // rows 16qb + 4G + i of key l16 into the pair's buffer
+      const auto pd = __builtin_bit_cast(v8s, pa);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const unsigned w0 = pw[2 * qb], w1 = pw[2 * qb + 1];
-        // lanes j, j ^ 1 swap 16-bit halves: lane j then holds rows 2t + (j & 1) (word t) of keys j & ~1, +1
-        const unsigned n0 = (unsigned)__builtin_amdgcn_update_dpp(0, (int)w0, 0xB1, 0xF, 0xF, false);
-        const unsigned n1 = (unsigned)__builtin_amdgcn_update_dpp(0, (int)w1, 0xB1, 0xF, 0xF, false);
-        const bool odd = j & 1;
-        const unsigned ra = odd ? (n0 >> 16) | (w0 & 0xFFFF0000u) : (w0 & 0xFFFFu) | (n0 << 16);
-        const unsigned rb = odd ? (n1 >> 16) | (w1 & 0xFFFF0000u) : (w1 & 0xFFFFu) | (n1 << 16);
-        // lanes j, j ^ 2 swap words: lane j then holds row j of keys 0..3
-        const bool low = j < 2;
-        const unsigned r = (unsigned)__builtin_amdgcn_update_dpp(0, (int)(low ? rb : ra), 0x4E, 0xF, 0xF, false);
-        ds_w[qb] = low ? v2u{ra, r} : v2u{r, rb};
-      }
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsst[pr * 512 + (16 * qb + 4 * G + i) * 16 + l16] = (us)pd[4 * qb + i];
       ds_qs0 = qs0;
       ds_h = h_c;
       ds_pending = true;
     }
     // dV += P^T dO ; dK += dS^T Q
+    if constexpr (STORE_DS) {
+      // the fragments of product dt + 1 are read while product dt runs (kept in that order by scheduling
+      // barriers: with the dS staging this instance holds more registers, and the compiler would
+      // otherwise read each fragment just before its product)
+      v8s bt = cat44(lds_read_tr_at(smem, tb), lds_read_tr_at(smem, tb + 32 * D));
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const int o1 = tb ^ (32 * dt);
-      const v8s bt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
-      acc[dt] = Elem<T>::mma16(pa, Elem<T>::cast(bt), acc[dt]);
+      for (int dt = 0; dt < D / 16; ++dt) {
+        v8s bn;
+        if (dt + 1 < D / 16) {
+          const int o1 = tb ^ (32 * (dt + 1));
+          bn = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[dt] = Elem<T>::mma16(pa, Elem<T>::cast(bt), acc[dt]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (dt + 1 < D / 16) bt = bn;
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const int o1 = tb ^ (32 * dt);
+        const v8s bt = cat44(lds_read_tr_at(smem, o1), lds_read_tr_at(smem, o1 + 32 * D));
+        acc[dt] = Elem<T>::mma16(pa, Elem<T>::cast(bt), acc[dt]);
+      }
     }
   }
 
@@ -1596,8 +1603,8 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
 // rows 32*(w%2) .. +31 and dQ columns 256*(w/2) .. +255, as dQ^T += K^T dS^T with 32x32x16 MFMAs (A = K^T
 // by transpose reads of the LDS tile, the same reads as the forward's V^T at D = 256; B = this lane's row
 // of dS, 8 keys per lane, 16 bytes straight from the workspace). Key tiles of 32 keys x 512 columns (two
-// 32 x 256 halves, 64 KB for the two-stage ring) stream through LDS; the dS operands of the next tile are
-// loaded beside its copy. dS is stored in a [q-head][query token][ds_ld] array; inside each 32-key block
+// 32 x 256 halves, 64 KB for the two-stage ring) stream through LDS; dS tiles go through a three-stage
+// LDS ring, copied two steps ahead, since they come from HBM rather than from the L2 that serves K. dS is stored in a [q-head][query token][ds_ld] array; inside each 32-key block
 // key 16a + 8c + 4h + j sits at position 16c + 8h + 4a + j, so that the lane (row, half h) of k-step c
 // reads one 16-byte run in the order the K^T operand delivers the keys. The dK/dV pass writes every
 // allowed pair; a tile that holds a pair outside the mask (or past the key range) replaces those dS
@@ -1608,7 +1615,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
   constexpr int TILE = BN * DH;             // 16-bit elements of one key half-tile
   constexpr int NDMA = TILE * 2 / 1024 / 4;  // 16-byte copies per wave per half
   static_assert(NDMA >= 1, "half tile must split over 4 waves");
+  constexpr int R = 3;            // dS stages: a tile's dS is copied R - 1 steps ahead (HBM latency)
+  constexpr int DST = BM * BN;    // 16-bit elements of one dS tile (64 rows x 32 keys, 64-byte rows)
   __shared__ __attribute__((aligned(1024))) us smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(1024))) us dsm[R * DST];
   const AttnShape& s = a.s;
   const bool packed = s.cu_q != nullptr;
   if (packed && *s.err) {
@@ -1636,13 +1646,16 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
 
   const us* kg = (const us*)a.k + seq_off(a.ak, packed, b, sq.tk0) + (int64_t)g * a.ak.head;
   const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;
-  // this lane's dS row (rows past the sequence end read the last row and are never stored), from the
-  // k-step's half 8*hh
-  const us* dsr = a.ds + ((int64_t)h * a.nrows + rowbase + min(qi, sq.sq - 1)) * a.ds_ld + 8 * hh;
-  auto load_ds = [&](int tile, v8s* d) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) d[c] = *reinterpret_cast<const v8s*>(dsr + tile * BN + 16 * c);
-  };
+  // dS tiles (the workgroup's 64 rows x 32 keys) are copied into an R-stage LDS ring, one 16-byte chunk
+  // per lane: row r = 16w + lane/4 takes physical chunk lane%4, which holds logical chunk (lane%4) ^
+  // ((r >> 2) & 3), so that the operand reads below (32 rows, one chunk each) spread over all banks.
+  // Rows past the sequence end copy the last row (never stored).
+  const us* dsbase = a.ds + ((int64_t)h * a.nrows + rowbase + q0) * a.ds_ld;
+  const int crow = 16 * w + (lane >> 2);
+  const unsigned coff = (unsigned)((min(crow, sq.sq - 1 - q0) * a.ds_ld + 8 * ((lane & 3) ^ ((crow >> 2) & 3))) * 2);
+  auto issue_ds = [&](int tile) { dma16(dsbase, coff + (unsigned)(tile * BN * 2), dsm + (tile % R) * DST + w * 512); };
+  // operand read of k-step c: row 32wr + lrow, logical chunk 2c + hh (keys 16c + 8hh .. +7 as stored)
+  const int orow = 32 * wr + lrow, oswz = (orow >> 2) & 3;
 
   const TileDma<DH, BN, NDMA, true, PAD> dma(w, lane, a.ak.row, a.ak.row, min(s.dqk, DH), max(0, s.dqk - DH));
   auto issue = [&](int tile, int stage) {
@@ -1668,25 +1681,32 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
     zero_lds<2 * 2 * TILE>(smem);
     __syncthreads();
   }
-  v8s dcur[2], dnext[2];
+  // copy order: K tile j + 1, then dS tile j + R - 1 (issued after the barrier of step j), so the wait
+  // that opens step j + 1 lets the last dS copy stay in flight (vmcnt(1)) whenever one was issued
+  bool ds_ahead = false;
   if (j0 < n_tiles) {
-    load_ds(j0, dcur);
     issue(j0, j0 & 1);
+#pragma unroll
+    for (int t = 0; t < R - 1; ++t)
+      if (j0 + t < n_tiles) issue_ds(j0 + t);
+    ds_ahead = j0 + 1 < n_tiles;
   }
   for (int j = j0; j < n_tiles; ++j) {
-    wait_vmem();
+    if (ds_ahead) wait_vmem_but1();
+    else wait_vmem();
     __syncthreads();
-    if (j + 1 < n_tiles) {
-      load_ds(j + 1, dnext);
-      issue(j + 1, (j + 1) & 1);
-    }
+    if (j + 1 < n_tiles) issue(j + 1, (j + 1) & 1);
+    ds_ahead = j + R - 1 < n_tiles;
+    if (ds_ahead) issue_ds(j + R - 1);
     const int kv0 = j * BN;
     const bool skip = !cols || (s.mask != 0 && kv0 > qw0 + 31 + delta) ||  // tile fully masked for this wave
                       (s.wl >= 0 && kv0 + BN - 1 < qw0 + delta - s.wl);      // tile before this wave's windows
     if (!skip) {
       const bool need_mask = (kv0 + BN > sq.skv) || (s.mask != 0 && kv0 + BN - 1 > qw0 + delta) ||
                              (s.wl >= 0 && kv0 < qw0 + 31 + delta - s.wl);
-      v8s d[2] = {dcur[0], dcur[1]};
+      v8s d[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) d[c] = lds_read16_at(dsm, 2 * ((j % R) * DST + orow * BN + 8 * ((2 * c + hh) ^ oswz)));
       if (need_mask) {  // one branch per tile: element e of k-step c is key kv0 + 16(e/4) + 8c + 4hh + e%4
         const int lim = min(sq.skv - 1, s.mask == 0 ? sq.skv : qi + delta) - kv0 - 4 * hh;
         const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);
@@ -1710,8 +1730,6 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
           acc[dt] = Elem<T>::mma32(Elem<T>::cast(cat44(lo, hi)), Elem<T>::cast(d[c]), acc[dt]);
         }
     }
-    dcur[0] = dnext[0];
-    dcur[1] = dnext[1];
   }
 
   if (cols && qi < sq.sq) {
@@ -2302,6 +2320,8 @@ static int bwd_t(const BwdArgs& a, int passes, hipStream_t st) {
     const dim3 grid(a.s.batch * a.s.hkv * a.n_kvtiles);
     if constexpr (D <= 256) {
       hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, dkdv_kb<D>(), bwd_minw<D>(), T, PAD>), grid, dim3(256), 0, st, a);
+    } else if (a.ds != nullptr) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, T, PAD, true>), grid, dim3(512), 0, st, a);
     } else {
       hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, T, PAD>), grid, dim3(512), 0, st, a);
     }

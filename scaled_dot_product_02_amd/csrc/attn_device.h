@@ -90,6 +90,9 @@ __device__ __forceinline__ v4s lds_read_tr(const unsigned short* base, int elem)
 __device__ __forceinline__ v8s lds_read16_at(const void* base, int byte_off) {
   return *reinterpret_cast<const v8s*>(static_cast<const char*>(base) + byte_off);
 }
+__device__ __forceinline__ v4s lds_read8_at(const void* base, int byte_off) {
+  return *reinterpret_cast<const v4s*>(static_cast<const char*>(base) + byte_off);
+}
 __device__ __forceinline__ v4s lds_read_tr_at(const void* base, int byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4s*)(static_cast<const char*>(base) + byte_off));

@@ -1282,22 +1282,21 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
 
   // stored-dS backward (STORE_DS, an instance of its own: the default one keeps its registers): the
   // role-1 wave of a pair puts the dS of an iteration (rounded to T: the values of its dK product) into
-  // its [32 row][16 key] LDS buffer and, after the next barrier, reads it back a row run per lane and
-  // writes it out, so that the copy wait before that barrier does not also wait for these stores and
-  // no register stays live across the S/dP products. Key 16a + 8c + 4h + j of a 32-key block goes to
-  // position 16c + 8h + 4a + j (the order attn_bwd_dq_ds_kernel reads); rows past the sequence end are
-  // not stored.
+  // its [32 row][16 key] LDS buffer and, after the next barrier, reads it back 8 keys of a row per lane
+  // and writes them out as one 16-byte run, so that the copy wait before that barrier does not also wait
+  // for these stores and no register stays live across the S/dP products. Key 16a + 8c + 4h + j of a
+  // 32-key block goes to position 16c + 8a + 4h + j (the order attn_bwd_dq_ds_kernel reads; a pair of
+  // waves holds one a); rows past the sequence end are not stored.
   int ds_qs0 = 0, ds_h = 0;
   bool ds_pending = false;
   auto store_ds = [&]() {
     if (!STORE_DS || !ds_pending) return;
-    const int r = lane >> 1, c = lane & 1;  // row r, keys 8c .. 8c + 7 of the pair (runs h = 0, 1)
+    const int r = lane >> 1, c = lane & 1;  // row r, keys 8c .. 8c + 7 of the pair
     const v8s x = *reinterpret_cast<const v8s*>(dsst + pr * 512 + r * 16 + 8 * c);
     if (ds_qs0 + r < sq.sq) {
       T* dsp = reinterpret_cast<T*>(a.ds) + ((int64_t)ds_h * a.nrows + rowbase + ds_qs0 + r) * a.ds_ld +
-               (kw0 - (kw0 & 31)) + 16 * c + 4 * ((kw0 >> 4) & 1);
-      __builtin_nontemporal_store(v4s{x[0], x[1], x[2], x[3]}, reinterpret_cast<v4s*>(dsp));
-      __builtin_nontemporal_store(v4s{x[4], x[5], x[6], x[7]}, reinterpret_cast<v4s*>(dsp + 8));
+               (kw0 - (kw0 & 31)) + 16 * c + 8 * ((kw0 >> 4) & 1);
+      *reinterpret_cast<v8s*>(dsp) = x;  // plain store: the two pairs' runs of a 32-byte sector merge in L2
     }
     ds_pending = false;
   };
@@ -1602,13 +1601,14 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dq_pair_kernel(BwdArgs a) {
 // Workgroup = 4 waves = 64 query rows of one (sequence, q-head), two workgroups per CU: wave w takes
 // rows 32*(w%2) .. +31 and dQ columns 256*(w/2) .. +255, as dQ^T += K^T dS^T with 32x32x16 MFMAs (A = K^T
 // by transpose reads of the LDS tile, the same reads as the forward's V^T at D = 256; B = this lane's row
-// of dS, 8 keys per lane, 16 bytes straight from the workspace). Key tiles of 32 keys x 512 columns (two
-// 32 x 256 halves, 64 KB for the two-stage ring) stream through LDS; dS tiles go through a three-stage
-// LDS ring, copied two steps ahead, since they come from HBM rather than from the L2 that serves K. dS is stored in a [q-head][query token][ds_ld] array; inside each 32-key block
-// key 16a + 8c + 4h + j sits at position 16c + 8h + 4a + j, so that the lane (row, half h) of k-step c
-// reads one 16-byte run in the order the K^T operand delivers the keys. The dK/dV pass writes every
-// allowed pair; a tile that holds a pair outside the mask (or past the key range) replaces those dS
-// values by zeros, whatever the workspace holds there.
+// of dS, 8 keys per lane). Key tiles of 32 keys x 512 columns (two 32 x 256 halves, 64 KB for the
+// two-stage ring) stream through LDS; dS tiles go through a three-stage LDS ring, copied two steps ahead,
+// since they come from HBM rather than from the L2 that serves K. dS is stored in a [q-head][query
+// token][ds_ld] array; inside each 32-key block key 16a + 8c + 4h + j sits at position 16c + 8a + 4h + j
+// (a 16-byte run per dK/dV wave pair), so the lane (row, half h) of k-step c takes two 8-byte pieces,
+// keys 8c + 4h + j and the same + 16, in the order the K^T operand delivers the keys. The dK/dV pass
+// writes every allowed pair; a tile that holds a pair outside the mask (or past the key range) replaces
+// those dS values by zeros, whatever the workspace holds there.
 template <typename T, bool PAD>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
   constexpr int DH = 256, BM = 64, BN = 32;
@@ -1654,7 +1654,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
   const int crow = 16 * w + (lane >> 2);
   const unsigned coff = (unsigned)((min(crow, sq.sq - 1 - q0) * a.ds_ld + 8 * ((lane & 3) ^ ((crow >> 2) & 3))) * 2);
   auto issue_ds = [&](int tile) { dma16(dsbase, coff + (unsigned)(tile * BN * 2), dsm + (tile % R) * DST + w * 512); };
-  // operand read of k-step c: row 32wr + lrow, logical chunk 2c + hh (keys 16c + 8hh .. +7 as stored)
+  // operand of k-step c: row 32wr + lrow, the 8-byte half hh of logical chunks 2c (keys 8c + 4hh + j) and
+  // 2c + 1 (the same + 16)
   const int orow = 32 * wr + lrow, oswz = (orow >> 2) & 3;
 
   const TileDma<DH, BN, NDMA, true, PAD> dma(w, lane, a.ak.row, a.ak.row, min(s.dqk, DH), max(0, s.dqk - DH));
@@ -1706,7 +1707,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_ds_kernel(BwdArgs a) {
                              (s.wl >= 0 && kv0 < qw0 + 31 + delta - s.wl);
       v8s d[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) d[c] = lds_read16_at(dsm, 2 * ((j % R) * DST + orow * BN + 8 * ((2 * c + hh) ^ oswz)));
+      for (int c = 0; c < 2; ++c) {
+        const int rb = 2 * ((j % R) * DST + orow * BN) + 8 * hh;
+        d[c] = cat44(lds_read8_at(dsm, rb + 16 * ((2 * c) ^ oswz)), lds_read8_at(dsm, rb + 16 * ((2 * c + 1) ^ oswz)));
+      }
       if (need_mask) {  // one branch per tile: element e of k-step c is key kv0 + 16(e/4) + 8c + 4hh + e%4
         const int lim = min(sq.skv - 1, s.mask == 0 ? sq.skv : qi + delta) - kv0 - 4 * hh;
         const int lo = s.wl >= 0 ? qi + delta - s.wl - kv0 - 4 * hh : -(1 << 30);

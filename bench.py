@@ -23,7 +23,8 @@ workload. The default run also times, under "cases", every other named case
 (tiny B1 H2 S128 D64 fp16; the packed GQA batch thd_d128; dense_d512; the two
 single-rank context-parallel shares at D=256 and D=512): forward, backward and
 combined ms, TFLOP/s and fraction of peak, compulsory-byte GB/s, per-kernel
-times, and the float64 oracle timed on a bounded slice of the same case. Under
+times, and the float64 oracle timed on a bounded slice of the same case (the D=512 cases also with the
+stored-dS backward, ATTN_FLAG_BWD_STORED_DS, under "stored_ds"). Under
 "extra" it reports attn_merge (two forward results combined, the ring step) on
 the dense D=128 query side against the HBM peak, and the HBM-bound
 short-sequence workload (B128 S256 D128), also with the 256 MB memory-side
@@ -50,9 +51,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "bab9fe12e640", "bytes": 863811757},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "2b18aae84e66", "bytes": 904160977},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "e59198264b6b", "bytes": 740881825},
+    ("dense_d128", "fwd"): {"fingerprint": "0a9e1bf8d1d9", "bytes": 867594855},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "5496dd2718de", "bytes": 911852754},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "a0dbc4ba3761", "bytes": 695809894},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
@@ -541,6 +542,31 @@ def single_pass_measure(w, steps, warmup):
                                 for n, e in kroof.items()}}
 
 
+def stored_ds_measure(w, steps, warmup):
+    """The same workload with the stored-dS backward (ATTN_FLAG_BWD_STORED_DS, head dims above 256): the
+    dK/dV pass also stores dS and the dQ pass is the product dS K. Backward ms and TFLOP/s (the same
+    credited FLOPs), per-kernel times, the dQ product's rate at its 2*D FLOP per pair, and the dS bytes
+    it stores and reads back (dtype, one per allowed pair and q-head)."""
+    r = run(w, steps, warmup, stored_ds=True)
+    fp = flop_per_pair(w)
+    km = r["kern_ms"]
+    bwd_ms = sum(t for n, t in km.items() if n != "fwd")
+    f_fwd, f_bwd = fp["fwd"] * r["pairs"], fp["bwd"] * r["pairs"]
+    f_dq = 2 * w.d * r["pairs"]
+    return {"what": "stored-dS backward (ATTN_FLAG_BWD_STORED_DS): preprocess, the dK/dV pass that also stores dS, "
+                    "dQ = scale * dS K",
+            "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2),
+                    "frac_of_peak": round(f_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4)},
+            "fwd_bwd": {"tflops": round((f_fwd + f_bwd) / ((km["fwd"] + bwd_ms) * 1e-3) / 1e12, 2),
+                        "frac_of_peak": round((f_fwd + f_bwd) / ((km["fwd"] + bwd_ms) * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+                        "ms_per_step": round(r["ms_step"], 4)},
+            "dq_product": {"tflops": round(f_dq / (km["bwd_dq"] * 1e-3) / 1e12, 2),
+                           "frac_of_peak": round(f_dq / (km["bwd_dq"] * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+                           "ds_bytes": int(2 * r["pairs"])},
+            "kernel_ms": {n: round(t, 4) for n, t in km.items()},
+            "kernel_ms_min": {n: round(t, 4) for n, t in r["kern_min"].items()}}
+
+
 def exp_split_measure(w, steps, warmup):
     """The same workload with the forward's exp split (ATTN_FLAG_FWD_EXP_SPLIT: a quarter of the exponentials
     on interior tiles by a VALU polynomial), the default backward: forward ms and TFLOP/s."""
@@ -569,6 +595,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-pass-only", action="store_true",
                     help="time only the workload with the single-pass backward and print its line")
+    ap.add_argument("--stored-ds-only", action="store_true",
+                    help="time only the workload with the stored-dS backward (heads above 256) and print its line")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other named cases and the informational merge and short-sequence lines")
     ap.add_argument("--merge-only", action="store_true",
@@ -606,6 +634,9 @@ def main():
     if args.single_pass_only:
         print(json.dumps({"workload": w.name, "single_pass": single_pass_measure(w, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.stored_ds_only:
+        print(json.dumps({"workload": w.name, "stored_ds": stored_ds_measure(w, args.steps, args.warmup)}), flush=True)
         return
     tele_before = telemetry() if not args.no_extra else None
     r = run(w, args.steps, args.warmup)
@@ -665,6 +696,8 @@ def main():
                 out["cases"][name]["graph_us_per_step"] = graph_step_us(wc)
             if atomic_supported(wc):
                 out["cases"][name]["single_pass"] = single_pass_measure(wc, max(5, args.steps // 2), 3)
+            if max(wc.d, wc.d_v) > 256:  # the stored-dS backward serves the heads above 256
+                out["cases"][name]["stored_ds"] = stored_ds_measure(wc, max(5, args.steps // 2), 3)
         out["extra"] = {"merge": merge_measure(w)}
         w3 = WORKLOADS["short_d128"]
         r3 = run(w3, max(5, args.steps // 3), 3)

@@ -146,9 +146,10 @@ typedef struct attn_problem {
  * flag. */
 #define ATTN_FLAG_FWD_EXP_SPLIT 2
 
-/* Stored-dS backward (pull request 3527, section Approach: dQ is the product of dS with K; section Known
- * limitations: the backward workspace there grows super-linearly, the price this mode pays too). With the
- * flag the dK/dV pass also stores dS = P * (dP - D), rounded to dtype, for every allowed (query, key) pair
+/* Stored-dS backward (pull request 3527, section Known limitations: the backward workspace there grows
+ * super-linearly with sequence length, the price this mode pays too; the default keeps it linear). dQ =
+ * scale * dS K is the gradient every backward here evaluates; with the flag the dK/dV pass also stores
+ * dS = P * (dP - D), rounded to dtype, for every allowed (query, key) pair
  * into the workspace, and the dQ pass becomes the product dQ = scale * dS K over each query row's allowed
  * keys, instead of recomputing S and dP (2 * head_dim FLOP per pair instead of 6 * head_dim). Results are
  * deterministic; dQ agrees with the default backward to the rounding of its summation order, dK and dV

@@ -59,34 +59,48 @@ __device__ __forceinline__ Seq seq_info(const AttnShape& s, int b) {
 // Query-side walk of the dK/dV passes: query tiles qt0 .. qt0+nq-1 of each q-head of a GQA group in
 // turn, one step per loaded tile. Running pointers to the tile's Q and dO rows and to the head's
 // lse2 / D rows replace a division and several 64-bit products per tile.
-template <int BQ>
-struct QueryWalk {
+template <int BQ, bool REV = false>
+struct QueryWalk {  // REV: each q-head's tiles from the last one down (the D = 512 dK/dV pass)
   const us *qh, *oh, *qp, *op;
   const float *l2, *rs;
   int64_t qstep, ostep, qhead, ohead, nrows;
   int qt, qt0, qt_end;
   __device__ __forceinline__ QueryWalk(const BwdArgs& a, bool packed, int b, const Seq& sq, int h0, int qt0_, int nq)
       : qstep((int64_t)BQ * a.aq.row), ostep((int64_t)BQ * a.ao.row), qhead(a.aq.head), ohead(a.ao.head),
-        nrows(a.nrows), qt(qt0_), qt0(qt0_), qt_end(qt0_ + nq) {
+        nrows(a.nrows), qt(REV ? qt0_ + nq - 1 : qt0_), qt0(qt0_), qt_end(qt0_ + nq) {
     qh = (const us*)a.q + seq_off(a.aq, packed, b, sq.tq0) + (int64_t)h0 * a.aq.head;
     oh = (const us*)a.d_o + seq_off(a.ao, packed, b, sq.tq0) + (int64_t)h0 * a.ao.head;
-    qp = qh + qt0 * qstep;
-    op = oh + qt0 * ostep;
+    qp = qh + qt * qstep;
+    op = oh + qt * ostep;
     const int64_t row0 = (int64_t)h0 * a.nrows + (packed ? sq.tq0 : (int64_t)b * a.s.sq);
     l2 = a.lse2 + row0;
     rs = a.rowsum + row0;
   }
   __device__ __forceinline__ void next() {
-    qp += qstep;
-    op += ostep;
-    if (++qt == qt_end) {  // next q-head of the group
-      qt = qt0;
-      qh += qhead;
-      oh += ohead;
-      qp = qh + qt0 * qstep;
-      op = oh + qt0 * ostep;
-      l2 += nrows;
-      rs += nrows;
+    if constexpr (REV) {
+      qp -= qstep;
+      op -= ostep;
+      if (qt-- == qt0) {  // next q-head of the group
+        qt = qt_end - 1;
+        qh += qhead;
+        oh += ohead;
+        qp = qh + qt * qstep;
+        op = oh + qt * ostep;
+        l2 += nrows;
+        rs += nrows;
+      }
+    } else {
+      qp += qstep;
+      op += ostep;
+      if (++qt == qt_end) {  // next q-head of the group
+        qt = qt0;
+        qh += qhead;
+        oh += ohead;
+        qp = qh + qt0 * qstep;
+        op = oh + qt0 * ostep;
+        l2 += nrows;
+        rs += nrows;
+      }
     }
   }
 };
@@ -1255,7 +1269,9 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = v4f{};
 
   const TileDma<D, BQ, NDMA, true, PAD> dma(w, lane, a.aq.row, a.ao.row, s.dqk, s.dv);
-  QueryWalk<BQ> ld(a, packed, b, sq, g * s.group, qt0, nq);
+  // query tiles from the last one down: the workgroups an XCD runs together (key blocks of one kv-head) then
+  // read the same Q/dO tile at about the same time, from L2, instead of each starting at its own diagonal
+  QueryWalk<BQ, true> ld(a, packed, b, sq, g * s.group, qt0, nq);
   const int qt_end = qt0 + nq;
   auto issue = [&](int stage) {
     const int qs0 = ld.qt * BQ;
@@ -1278,7 +1294,7 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
   float* pbuf = xch + pr * 2 * 64 * 4;
   const int64_t rowbase = packed ? sq.tq0 : (int64_t)b * s.sq;  // the sequence's first query token
 
-  int qt_c = qt0, hq_c = g * s.group;  // query tile and q-head of the iteration
+  int qt_c = qt_end - 1, hq_c = g * s.group;  // query tile and q-head of the iteration (tiles walked downwards)
 
   // stored-dS backward (STORE_DS, an instance of its own: the default one keeps its registers): the
   // role-1 wave of a pair puts the dS of an iteration (rounded to T: the values of its dK product) into
@@ -1320,11 +1336,11 @@ __global__ void __launch_bounds__(512, 1) attn_bwd_dkdv_pair_kernel(BwdArgs a) {
     const float* l2s = reinterpret_cast<const float*>(dos + QTILE);
     const float* rss = l2s + 64;
     const int qs0 = qt_c * BQ, h_c = hq_c;
-    if (qt_c + 1 == qt_end) {
-      qt_c = qt0;
+    if (qt_c == qt0) {
+      qt_c = qt_end - 1;
       ++hq_c;
     } else {
-      ++qt_c;
+      --qt_c;
     }
     const bool active = kw0 < sq.skv && (s.mask == 0 || qs0 + BQ - 1 + delta >= kw0) &&
                         (s.wl < 0 || qs0 + delta - s.wl <= kw0 + KW - 1);

@@ -51,9 +51,9 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 # copy of known size (profiles/dense_d128_hbm_traffic.md). Each entry is valid only for the kernel it was
 # measured on: "traffic" is null once that kernel's source fingerprint (kernel_fingerprint) has changed.
 TRAFFIC = {
-    ("dense_d128", "fwd"): {"fingerprint": "0a9e1bf8d1d9", "bytes": 867594855},
-    ("dense_d128", "bwd_dq"): {"fingerprint": "5496dd2718de", "bytes": 911852754},
-    ("dense_d128", "bwd_dkdv"): {"fingerprint": "a0dbc4ba3761", "bytes": 695809894},
+    ("dense_d128", "fwd"): {"fingerprint": "244e429d5eb0", "bytes": 852121147},
+    ("dense_d128", "bwd_dq"): {"fingerprint": "c7bbbc9b6b9e", "bytes": 915104803},
+    ("dense_d128", "bwd_dkdv"): {"fingerprint": "56ff48a21ae8", "bytes": 693965439},
 }
 KERNEL_OF = {"fwd": "attn_fwd_kernel", "bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}
 

@@ -347,9 +347,11 @@ NOALLOC_MAX_WORKSPACE = 16 << 20  # ATTN_NOALLOC_MAX_WORKSPACE
 
 
 def attn_bwd_noalloc(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqlens_q=None, cu_seqlens_kv=None,
-                     max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, stream=None, window_left=-1):
+                     max_seqlen_q=None, max_seqlen_kv=None, dq=None, dk=None, dv=None, stream=None, window_left=-1,
+                     stored_ds=False):
     """attn_bwd_noalloc through the C-ABI: attn_bwd with the library's own per-device scratch array as the
     workspace (no workspace argument; problems needing more than NOALLOC_MAX_WORKSPACE bytes are declined).
+    ``stored_ds`` sets ATTN_FLAG_BWD_STORED_DS as in attn_bwd (its dS array must fit the scratch array too).
     Returns (dQ, dK, dV); dQ/dK/dV are allocated here unless given (the library allocates nothing)."""
     import torch
     _check_tensors(q, k, v, cu_seqlens_q is not None, cu_seqlens_q, cu_seqlens_kv, o=o, do=do, lse=lse, dq=dq,
@@ -365,7 +367,7 @@ def attn_bwd_noalloc(q, k, v, o, do, lse, mask="causal_tl", scale=None, cu_seqle
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("dQ/dK/dV must have the strides of Q/K/V")
     p = make_problem(q, k, v, o, mask, scale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
-                     window_left)
+                     window_left, FLAG_BWD_STORED_DS if stored_ds else 0)
     st = lib().attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                 _ptr(dk), _ptr(dv), _stream(stream))
     if st != 0:

@@ -54,6 +54,27 @@ def test_noalloc_matches_attn_bwd_on_two_calls_the_second_smaller():
         assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
 
 
+def test_noalloc_stored_ds_matches_attn_bwd():
+    """The stored-dS backward on the library's array (its dS lives there too): two calls in a row, the second
+    smaller and packed, each equal to attn_bwd with the flag and a caller workspace, bit for bit."""
+    cases = [
+        small("noalloc_sds_big", batch=1, hq=4, hkv=2, sq=300, skv=300, d=512, dtype="bf16", mask="causal_tl",
+              seed=43),
+        small("noalloc_sds_small", hq=2, hkv=1, d=264, dv=512, dtype="fp16", mask="causal_br", seed=44,
+              seqlens=(40, 1, 77), seqlens_kv=(60, 5, 77)),
+    ]
+    for w in cases:
+        print(f"noalloc stored-dS case {w.name}", flush=True)
+        x, q, k, v, do, kw = _inputs(w)
+        o, lse = sd.attn_fwd(q, k, v, **kw)
+        ref = sd.attn_bwd(q, k, v, o, do, lse, dq=_nan(q), dk=_nan(k), dv=_nan(v), stored_ds=True, **kw)
+        got = sd.attn_bwd_noalloc(q, k, v, o, do, lse, dq=_nan(q), dk=_nan(k), dv=_nan(v), stored_ds=True, **kw)
+        torch.cuda.synchronize()
+        for n, a, b in zip(("dQ", "dK", "dV"), ref, got):
+            assert torch.isfinite(b).all(), f"{w.name}: {n} has unwritten elements"
+            assert torch.equal(a, b), f"{w.name}: attn_bwd_noalloc differs from attn_bwd in {n}"
+
+
 def test_noalloc_declines_problems_beyond_its_array():
     # 2 x 262144 query rows x 8 heads x 8 bytes = 32 MiB of row arrays, beyond the 16 MiB array
     q = torch.empty(2, 262144, 8, 64, dtype=torch.bfloat16, device=DEV)

@@ -5,7 +5,7 @@ bottom-right; causal masks with or without a sliding window), MHA or GQA, and ei
 independent query and key lengths (1 .. 500, so bottom-right cases with more queries than keys have
 empty rows) or a packed batch of 1-4 sequences with lengths 0 .. 400 (empty sequences included).
 Acceptance is parity_util.compare (2 x floor and the fixed bounds), every output NaN-prefilled and
-required to be written.
+required to be written. The configurations with a head above 256 also run through the stored-dS backward.
 """
 
 import numpy as np
@@ -65,4 +65,15 @@ def _id(kw):
 def test_fuzz(i):
     w = small(f"fuzz_{i}", **CASES[i])
     ok, msgs = run_and_check(w)
+    assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))
+
+
+WIDE = [i for i, c in enumerate(CASES) if max(c["d"], c["dv"]) > 256]
+
+
+@pytest.mark.parametrize("i", WIDE, ids=[f"{i}-{_id(CASES[i])}" for i in WIDE])
+def test_fuzz_stored_ds(i):
+    """The same configurations with a head above 256 through the stored-dS backward (ATTN_FLAG_BWD_STORED_DS)."""
+    w = small(f"fuzz_sds_{i}", **CASES[i])
+    ok, msgs = run_and_check(w, stored_ds=True)
     assert ok, "\n".join(m for m in msgs if m.startswith("FAIL"))

@@ -498,6 +498,15 @@ def test_stored_ds_flag(L):
     both = dense_problem(d=512)
     both.flags = B.FLAG_BWD_STORED_DS | B.FLAG_BWD_ATOMIC_DQ
     expect(L, bwd(L, both), UNSUPPORTED, "head dims up to 128")
+    # the dQ product addresses a workgroup's dS rows with 32-bit offsets: key lengths stay below 2^24
+    long_keys = dense_problem(b=1, sq=64, skv=(1 << 24) - 8, hq=1, hkv=1, d=512)
+    long_keys.flags = B.FLAG_BWD_STORED_DS
+    far = [(1 << 44) + i * (1 << 40) for i in range(10)]  # buffers 1 TiB apart: no extent overlaps
+    expect(L, bwd(L, long_keys, *far[:9], ws=far[9], ws_bytes=1 << 62), UNSUPPORTED, "key lengths below 2^24")
+    # a dS array beyond 2^62 bytes is declined when the problem is checked (workspace size 0)
+    huge = dense_problem(b=1 << 16, sq=1 << 16, skv=1 << 20, hq=64, hkv=64, d=512)
+    huge.flags = B.FLAG_BWD_STORED_DS
+    assert L.attn_bwd_workspace_bytes(ctypes.byref(huge)) == 0
     # the forward ignores the flag: no workspace change
     p0 = dense_problem(b=2, sq=256, skv=300, hq=4, hkv=2, d=512)
     f0 = L.attn_fwd_workspace_bytes(ctypes.byref(p0))
